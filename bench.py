@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8 fine-grained quantization + block-scaled GEMM hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+    1. online 1x128 activation quantization of X (BF16 -> E4M3 codes + FP32 tile scales)
+    2. online 128x128 weight quantization of W (BF16 -> E4M3 codes + FP32 block scales;
+       weights change every training step, so they are quantized every step)
+    3. block-scaled FP8 GEMM C = X W^T with FP32 promotion every 128 K (BF16 or FP32 out),
+       grouped over experts for the MoE workloads.
+Default workload: the dense projection X[4096x7168] x W[7168x7168]^T, BF16 out.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense|large|moe_up|moe_down]
+
+Prints ONE JSON line.  `value` = 2*M*N*K*steps / (timed wall time of the steps), i.e. GEMM
+TFLOP/s including both online quantizers.  Inputs are resident in HBM before timing.  To
+keep the 256 MB Infinity Cache from serving repeated steps, steps rotate over several
+buffer sets (together larger than the cache).  Per-kernel durations come from HIP events
+recorded on the stream the kernels run on.  `roofline` describes the dominant kernel (the
+GEMM): algorithmic FLOPs per launch / its average duration, against the 5.0 PFLOP/s dense
+FP8 peak.  `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "FP8 block-scaled GEMM TFLOP/s incl. online quant; % FP8 MFMA peak; quant GB/s"
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+GEMM_SOURCE = os.path.join(ROOT, "fp8_fine_grained_fp8q_amd", "csrc", "gemm.hip")
+
+WORKLOADS = {
+    "dense": "dense projection X[4096x7168] . W[7168x7168]^T, bf16 out",
+    "large": "large fused pipeline X[16384x7168] (Student-t 3) . W[18432x7168]^T, fp32 out",
+    "moe_up": "MoE up-projection, 32 local experts of 256 (top-8 routing of 8192 tokens), W[32][4096x7168], bf16 out",
+    "moe_down": "MoE down-projection, 32 local experts, SiLU(g)*u inputs [n x 2048], W[32][7168x2048], bf16 out",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dense", choices=sorted(WORKLOADS))
+    ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0: enough to exceed the 256 MB cache)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 256 MiB device copy per step (untimed) for counter calibration")
+    return ap.parse_args()
+
+
+def gen(workload: str):
+    import workloads as wl
+    return wl.CONFIGS[workload]()
+
+
+def source_hash() -> str:
+    with open(GEMM_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per GEMM launch from the committed counter summary, only if it was taken on
+    the current GEMM source and this workload; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("gemm_source_sha256_16") != source_hash() or t.get("workload") != workload:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, flops_step):
+    """The oracle as it stands, on a bounded sample of the workload (rank 0 only)."""
+    from oracle import gemm as og
+    from oracle import quant as oq
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    x, w, offsets = cfg["x"], cfg["w"], cfg["offsets"]
+    M, K = x.shape
+    G, N, _ = w.shape
+    if offsets is None:
+        R = min(M, 512)
+        t0 = time.perf_counter()
+        xq, sa = oq.quantize_act_1x128(x[:R])
+        t1 = time.perf_counter()
+        wq, sb = oq.quantize_w_128x128(w[0])
+        t2 = time.perf_counter()
+        og.gemm_blockscaled(xq, sa, wq, sb)
+        t3 = time.perf_counter()
+        scale = M / R
+        t_step = (t1 - t0) * scale + (t2 - t1) + (t3 - t2) * scale
+        sample = (f"oracle on rows 0..{R - 1} of X (act quant + GEMM against all {N} columns, "
+                  f"extrapolated x{scale:g} to {M} rows) plus the full weight quantization")
+    else:
+        g = 0
+        while offsets[g + 1] == offsets[g]:
+            g += 1
+        lo, hi = int(offsets[g]), int(offsets[g + 1])
+        t0 = time.perf_counter()
+        xq, sa = oq.quantize_act_1x128(x[lo:hi])
+        t1 = time.perf_counter()
+        wq, sb = oq.quantize_w_128x128(w[g])
+        t2 = time.perf_counter()
+        og.gemm_blockscaled(xq, sa, wq, sb)
+        t3 = time.perf_counter()
+        rows_scale = M / (hi - lo)
+        t_step = (t1 - t0) * rows_scale + (t2 - t1) * G + (t3 - t2) * rows_scale
+        sample = (f"oracle on expert {g} ({hi - lo} rows): act quant and GEMM extrapolated x{rows_scale:.3g} "
+                  f"to {M} rows, weight quant x{G} experts")
+    return {"value": flops_step / t_step / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": sample, "seconds_measured": round(t3 - t0, 2), "seconds_per_step_extrapolated": round(t_step, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import fp8_fine_grained_fp8q_amd as fq
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fq.load_library()
+    dev = torch.device("cuda:0")
+
+    t_gen = time.perf_counter()
+    cfg = gen(args.workload)
+    x_np, w_np, offsets_np = cfg["x"], cfg["w"], cfg["offsets"]
+    M, K = x_np.shape
+    G, N, _ = w_np.shape
+    grouped = offsets_np is not None
+    out_dtype = torch.float32 if cfg["out_dtype"] == "f32" else torch.bfloat16
+    print(f"[bench] workload {args.workload}: M={M} N={N} K={K} G={G} generated in "
+          f"{time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+
+    flops = 2.0 * M * N * K
+    bytes_act = 2 * M * K + M * K + 4 * M * (K // 128)
+    bytes_w = G * (2 * N * K + N * K + 4 * (N // 128) * (K // 128))
+    out_bytes = M * N * (4 if out_dtype == torch.float32 else 2)
+    bytes_gemm = M * K + 4 * M * (K // 128) + G * (N * K + 4 * (N // 128) * (K // 128)) + out_bytes
+
+    x0 = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    w0 = torch.from_numpy(w_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    w0 = w0 if grouped else w0[0]
+    off_d = torch.from_numpy(offsets_np).to(dev) if grouped else None
+    per_set = 2 * x0.numel() + 2 * w0.numel() + M * K + G * N * K + out_bytes
+    nsets = args.sets or max(2, int(np.ceil(3 * 256e6 / per_set)))
+    nsets = min(nsets, 8)
+    sets = []
+    for i in range(nsets):
+        xs = x0 if i == 0 else x0.clone()
+        ws = w0 if i == 0 else w0.clone()
+        sets.append({
+            "x": xs, "w": ws,
+            "xq": torch.empty((M, K), dtype=torch.uint8, device=dev),
+            "sa": torch.empty((K // 128, M), dtype=torch.float32, device=dev),
+            "wq": torch.empty(ws.shape, dtype=torch.uint8, device=dev),
+            "sb": torch.empty(((G,) if grouped else ()) + (N // 128, K // 128), dtype=torch.float32, device=dev),
+            "c": torch.empty((M, N), dtype=out_dtype, device=dev),
+        })
+    cal_src = cal_dst = None
+    if args.copy_calibration:
+        cal_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        cal_dst = torch.empty_like(cal_src)
+
+    stream = torch.cuda.current_stream()
+
+    def step(s):
+        fq.fp8q_quantize_act_1x128(s["x"], xq=s["xq"], sa=s["sa"], stream=stream)
+        fq.fp8q_quantize_w_128x128(s["w"], wq=s["wq"], sb=s["sb"], stream=stream)
+        if grouped:
+            fq.fp8q_grouped_gemm_blockscaled(s["xq"], s["sa"], s["wq"], s["sb"], off_d, out=s["c"], stream=stream)
+        else:
+            fq.fp8q_gemm_blockscaled(s["xq"], s["sa"], s["wq"], s["sb"], out=s["c"], stream=stream)
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+        if cal_src is not None:
+            cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+
+    K_steps = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K_steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K_steps):
+        s = sets[i % nsets]
+        e = evs[i]
+        e[0].record(stream)
+        fq.fp8q_quantize_act_1x128(s["x"], xq=s["xq"], sa=s["sa"], stream=stream)
+        e[1].record(stream)
+        fq.fp8q_quantize_w_128x128(s["w"], wq=s["wq"], sb=s["sb"], stream=stream)
+        e[2].record(stream)
+        if grouped:
+            fq.fp8q_grouped_gemm_blockscaled(s["xq"], s["sa"], s["wq"], s["sb"], off_d, out=s["c"], stream=stream)
+        else:
+            fq.fp8q_gemm_blockscaled(s["xq"], s["sa"], s["wq"], s["sb"], out=s["c"], stream=stream)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if cal_src is not None:
+        for _ in range(3):
+            cal_dst.copy_(cal_src)
+        torch.cuda.synchronize()
+
+    t_act = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in range(K_steps)]) * 1e-3
+    t_w = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in range(K_steps)]) * 1e-3
+    t_g = np.array([evs[i][2].elapsed_time(evs[i][3]) for i in range(K_steps)]) * 1e-3
+    t_dev = evs[0][0].elapsed_time(evs[-1][3]) * 1e-3
+    ms_per_step = wall / K_steps * 1e3
+    value = flops * K_steps / wall / 1e12
+
+    a_act, a_w, a_g = t_act.mean(), t_w.mean(), t_g.mean()
+    gemm_tflops = flops / a_g / 1e12
+    traffic = measured_traffic(args.workload)
+    roofline = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
+                "kernel": "gemm_blockscaled_kernel<%s>" % ("true" if grouped else "false"),
+                "flop_per_launch": flops, "avg_launch_us": round(a_g * 1e6, 2),
+                "algorithmic_bytes_per_launch": bytes_gemm}
+    if grouped:
+        # the expert-weight stream bounds the grouped GEMM: report the HBM view as well
+        roofline["hbm_achieved_GBs"] = round(bytes_gemm / a_g / 1e9, 1)
+        roofline["hbm_frac"] = round(bytes_gemm / a_g / 1e9 / PEAK_HBM_GBS, 4)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic (seeded; shapes and distributions of the workload, no dataset)",
+        "config": {"workload": WORKLOADS[args.workload], "M": M, "N": N, "K": K, "experts": G,
+                   "out": cfg["out_dtype"], "buffer_sets": nsets},
+        "pct_fp8_peak_step": round(value / PEAK_FP8_TFLOPS * 100, 2),
+        "gemm_only_tflops": round(gemm_tflops, 1),
+        "kernels_us": {"quantize_act_1x128": round(a_act * 1e6, 2), "quantize_w_128x128": round(a_w * 1e6, 2),
+                       "gemm": round(a_g * 1e6, 2), "device_span_per_step": round(t_dev / K_steps * 1e6, 2)},
+        "quant_GBs": {"act": round(bytes_act / a_act / 1e9, 1), "act_frac_hbm": round(bytes_act / a_act / 1e9 / PEAK_HBM_GBS, 4),
+                      "w": round(bytes_w / a_w / 1e9, 1), "w_frac_hbm": round(bytes_w / a_w / 1e9 / PEAK_HBM_GBS, 4)},
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline and int(os.environ.get("RANK", "0")) == 0:
+        line["cpu_baseline"] = cpu_baseline(cfg, flops)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,174 @@
+"""Python binding of libfp8q: online fine-grained E4M3 quantization and block-scaled FP8
+GEMMs on AMD Instinct MI355X (gfx950).
+
+The functions below carry the names of the C ABI (include/fp8q.h) and only marshal
+arguments: PyTorch provides device memory and the current stream, every step of the
+computation runs in the library's HIP kernels.  There is no fallback: if the library is
+missing or no GPU is present the calls raise.
+
+    xq, sa = fp8q_quantize_act_1x128(x)            # x: bf16 [M, K] on cuda
+    wq, sb = fp8q_quantize_w_128x128(w)            # w: bf16 [G, N, K] or [N, K]
+    c = fp8q_gemm_blockscaled(xq, sa, wq, sb)      # bf16 [M, N] (or out_dtype=torch.float32)
+    c = fp8q_grouped_gemm_blockscaled(xq, sa, wq, sb, offsets)   # offsets: int32 [G+1] on cuda
+
+Layouts: xq uint8 [M, K]; sa float32 [K/128, M]; wq uint8 [G, N, K]; sb float32
+[G, N/128, K/128]; C row-major [M, N].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfp8q.so")
+
+FP8Q_OK = 0
+FP8Q_OUT_BF16 = 0
+FP8Q_OUT_F32 = 1
+ABI_VERSION = 1
+
+EXPORTED = ("fp8q_quantize_act_1x128", "fp8q_quantize_w_128x128", "fp8q_gemm_blockscaled",
+            "fp8q_grouped_gemm_blockscaled", "fp8q_status_string", "fp8q_abi_version")
+
+
+class Fp8qError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfp8q.so (built by fp8_fine_grained_fp8q_amd.build) and declare its C ABI."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libfp8q.so not found at {path}; build it with "
+                           "`python -m fp8_fine_grained_fp8q_amd.build`")
+    lib = ctypes.CDLL(path)
+    i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32
+    lib.fp8q_quantize_act_1x128.argtypes = [vp, i64, i64, vp, vp, vp]
+    lib.fp8q_quantize_w_128x128.argtypes = [vp, i64, i64, i64, vp, vp, vp]
+    lib.fp8q_gemm_blockscaled.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i32, vp]
+    lib.fp8q_grouped_gemm_blockscaled.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp]
+    for name in ("fp8q_quantize_act_1x128", "fp8q_quantize_w_128x128", "fp8q_gemm_blockscaled",
+                 "fp8q_grouped_gemm_blockscaled"):
+        getattr(lib, name).restype = i32
+    lib.fp8q_status_string.argtypes = [i32]
+    lib.fp8q_status_string.restype = ctypes.c_char_p
+    lib.fp8q_abi_version.argtypes = []
+    lib.fp8q_abi_version.restype = i32
+    if lib.fp8q_abi_version() != ABI_VERSION:
+        raise RuntimeError("libfp8q ABI version mismatch; rebuild the library")
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().fp8q_status_string(int(status)).decode()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _check(status: int, what: str):
+    if status != FP8Q_OK:
+        raise Fp8qError(status, what)
+
+
+def _need(t: torch.Tensor, dtype, name: str):
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} CUDA tensor")
+
+
+def fp8q_quantize_act_1x128(x: torch.Tensor, xq: torch.Tensor | None = None,
+                            sa: torch.Tensor | None = None, stream=None):
+    """1x128 activation tiles -> (xq uint8 [M, K], sa float32 [K/128, M])."""
+    _need(x, torch.bfloat16, "x")
+    M, K = x.shape
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if sa is None:
+        sa = torch.empty((K // 128, M), dtype=torch.float32, device=x.device)
+    _check(load_library().fp8q_quantize_act_1x128(_ptr(x), M, K, _ptr(xq), _ptr(sa), _stream(stream)),
+           "fp8q_quantize_act_1x128")
+    return xq, sa
+
+
+def fp8q_quantize_w_128x128(w: torch.Tensor, wq: torch.Tensor | None = None,
+                            sb: torch.Tensor | None = None, stream=None):
+    """128x128 weight blocks of w [G, N, K] (or [N, K]) -> (wq uint8, sb float32 [G, N/128, K/128])."""
+    _need(w, torch.bfloat16, "w")
+    squeeze = w.dim() == 2
+    G, N, K = (1, *w.shape) if squeeze else w.shape
+    if wq is None:
+        wq = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    if sb is None:
+        shape = (N // 128, K // 128) if squeeze else (G, N // 128, K // 128)
+        sb = torch.empty(shape, dtype=torch.float32, device=w.device)
+    _check(load_library().fp8q_quantize_w_128x128(_ptr(w), G, N, K, _ptr(wq), _ptr(sb), _stream(stream)),
+           "fp8q_quantize_w_128x128")
+    return wq, sb
+
+
+def _out_code(out_dtype) -> int:
+    if out_dtype == torch.bfloat16:
+        return FP8Q_OUT_BF16
+    if out_dtype == torch.float32:
+        return FP8Q_OUT_F32
+    raise ValueError("out_dtype must be torch.bfloat16 or torch.float32")
+
+
+def fp8q_gemm_blockscaled(xq, sa, wq, sb, out_dtype=torch.bfloat16, out: torch.Tensor | None = None,
+                          stream=None):
+    """C = dequant(xq, sa) @ dequant(wq, sb)^T with FP32 promotion per 128-wide K block."""
+    _need(xq, torch.uint8, "xq")
+    _need(wq, torch.uint8, "wq")
+    _need(sa, torch.float32, "sa")
+    _need(sb, torch.float32, "sb")
+    M, K = xq.shape
+    N = wq.shape[-2]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=xq.device)
+    _check(load_library().fp8q_gemm_blockscaled(_ptr(xq), _ptr(sa), _ptr(wq), _ptr(sb), M, N, K, _ptr(out),
+                                                _out_code(out.dtype), _stream(stream)),
+           "fp8q_gemm_blockscaled")
+    return out
+
+
+def fp8q_grouped_gemm_blockscaled(xq, sa, wq, sb, offsets, out_dtype=torch.bfloat16,
+                                  out: torch.Tensor | None = None, stream=None):
+    """Grouped (MoE): rows offsets[g]..offsets[g+1]-1 use expert g's weights wq[g], sb[g]."""
+    _need(xq, torch.uint8, "xq")
+    _need(wq, torch.uint8, "wq")
+    _need(sa, torch.float32, "sa")
+    _need(sb, torch.float32, "sb")
+    _need(offsets, torch.int32, "offsets")
+    M, K = xq.shape
+    G, N, _ = wq.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=xq.device)
+    _check(load_library().fp8q_grouped_gemm_blockscaled(
+        _ptr(xq), _ptr(sa), _ptr(wq), _ptr(sb), _ptr(offsets), G, M, N, K, _ptr(out),
+        _out_code(out.dtype), _stream(stream)), "fp8q_grouped_gemm_blockscaled")
+    return out
+
+
+quantize_act_1x128 = fp8q_quantize_act_1x128
+quantize_w_128x128 = fp8q_quantize_w_128x128
+gemm_blockscaled = fp8q_gemm_blockscaled
+grouped_gemm_blockscaled = fp8q_grouped_gemm_blockscaled

@@ -1,0 +1,110 @@
+// C ABI of libfp8q (see include/fp8q.h): argument checks, then one kernel launch per call.
+// Every check runs before the first HIP call, so a bad call never touches the device.
+#include "fp8q.h"
+
+#include <hip/hip_runtime.h>
+
+#include "fp8q_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 31;
+constexpr int64_t kMaxElems = int64_t(1) << 62;
+
+bool misaligned(const void *p, uintptr_t a = 16) { return (reinterpret_cast<uintptr_t>(p) % a) != 0; }
+
+bool bad_dim(int64_t v) { return v < 0 || v >= kMaxDim; }
+
+bool too_many(int64_t a, int64_t b) { return a != 0 && b > kMaxElems / a; }
+
+fp8q_status device_ok() {
+  int dev = 0;
+  return hipGetDevice(&dev) == hipSuccess ? FP8Q_OK : FP8Q_ERR_DEVICE;
+}
+
+fp8q_status launched(hipError_t e) { return e == hipSuccess ? FP8Q_OK : FP8Q_ERR_LAUNCH; }
+
+hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+// Shared checks of the two GEMM entry points (everything except the grouped extras).
+fp8q_status check_gemm(const uint8_t *xq, const float *sa, const uint8_t *wq, const float *sb,
+                       int64_t M, int64_t N, int64_t K, void *c, int32_t out_dtype) {
+  if (out_dtype != FP8Q_OUT_BF16 && out_dtype != FP8Q_OUT_F32) return FP8Q_ERR_DTYPE;
+  if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return FP8Q_ERR_SHAPE;
+  if (K < 128 || K % 128 != 0 || N % 128 != 0) return FP8Q_ERR_SHAPE;
+  if (too_many(M, K) || too_many(N, K) || too_many(M, N)) return FP8Q_ERR_SHAPE;
+  if (M == 0 || N == 0) return 1;  // nothing to do (positive: caller returns FP8Q_OK)
+  if (!xq || !sa || !wq || !sb || !c) return FP8Q_ERR_NULL;
+  if (misaligned(xq) || misaligned(sa) || misaligned(wq) || misaligned(sb) || misaligned(c))
+    return FP8Q_ERR_ALIGN;
+  return FP8Q_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fp8q_status fp8q_quantize_act_1x128(const uint16_t *x_bf16, int64_t M, int64_t K, uint8_t *xq,
+                                    float *sa, void *stream) {
+  if (bad_dim(M) || bad_dim(K) || K % 128 != 0 || too_many(M, K)) return FP8Q_ERR_SHAPE;
+  if (M == 0 || K == 0) return FP8Q_OK;
+  if (!x_bf16 || !xq || !sa) return FP8Q_ERR_NULL;
+  if (misaligned(x_bf16) || misaligned(xq) || misaligned(sa)) return FP8Q_ERR_ALIGN;
+  if (device_ok() != FP8Q_OK) return FP8Q_ERR_DEVICE;
+  return launched(fp8q::launch_quant_act(x_bf16, M, K, xq, sa, as_stream(stream)));
+}
+
+fp8q_status fp8q_quantize_w_128x128(const uint16_t *w_bf16, int64_t G, int64_t N, int64_t K,
+                                    uint8_t *wq, float *sb, void *stream) {
+  if (G < 1 || bad_dim(G) || bad_dim(N) || bad_dim(K)) return FP8Q_ERR_SHAPE;
+  if (N % 128 != 0 || K % 128 != 0) return FP8Q_ERR_SHAPE;
+  if (too_many(G, N) || too_many(G * N, K)) return FP8Q_ERR_SHAPE;
+  if (N == 0 || K == 0) return FP8Q_OK;
+  if (!w_bf16 || !wq || !sb) return FP8Q_ERR_NULL;
+  if (misaligned(w_bf16) || misaligned(wq) || misaligned(sb)) return FP8Q_ERR_ALIGN;
+  if (device_ok() != FP8Q_OK) return FP8Q_ERR_DEVICE;
+  return launched(fp8q::launch_quant_w(w_bf16, G, N, K, wq, sb, as_stream(stream)));
+}
+
+fp8q_status fp8q_gemm_blockscaled(const uint8_t *xq, const float *sa, const uint8_t *wq,
+                                  const float *sb, int64_t M, int64_t N, int64_t K, void *c,
+                                  int32_t out_dtype, void *stream) {
+  const fp8q_status st = check_gemm(xq, sa, wq, sb, M, N, K, c, out_dtype);
+  if (st != FP8Q_OK) return st > 0 ? FP8Q_OK : st;
+  if (device_ok() != FP8Q_OK) return FP8Q_ERR_DEVICE;
+  return launched(fp8q::launch_gemm(xq, sa, wq, sb, M, N, K, c, out_dtype == FP8Q_OUT_F32,
+                                    as_stream(stream)));
+}
+
+fp8q_status fp8q_grouped_gemm_blockscaled(const uint8_t *xq, const float *sa, const uint8_t *wq,
+                                          const float *sb, const int32_t *offsets, int64_t G,
+                                          int64_t M_tot, int64_t N, int64_t K, void *c,
+                                          int32_t out_dtype, void *stream) {
+  if (G < 1 || bad_dim(G)) return FP8Q_ERR_SHAPE;
+  const fp8q_status st = check_gemm(xq, sa, wq, sb, M_tot, N, K, c, out_dtype);
+  if (st < 0) return st;
+  if (too_many(G, N) || too_many(G * N, K)) return FP8Q_ERR_SHAPE;
+  if (st > 0) return FP8Q_OK;
+  if (!offsets) return FP8Q_ERR_NULL;
+  if (misaligned(offsets, 4)) return FP8Q_ERR_ALIGN;
+  if (device_ok() != FP8Q_OK) return FP8Q_ERR_DEVICE;
+  return launched(fp8q::launch_grouped_gemm(xq, sa, wq, sb, offsets, G, M_tot, N, K, c,
+                                            out_dtype == FP8Q_OUT_F32, as_stream(stream)));
+}
+
+const char *fp8q_status_string(fp8q_status status) {
+  switch (status) {
+    case FP8Q_OK: return "ok";
+    case FP8Q_ERR_NULL: return "null pointer argument";
+    case FP8Q_ERR_SHAPE: return "invalid shape (negative, K/N not a multiple of 128, G < 1, or too large)";
+    case FP8Q_ERR_ALIGN: return "misaligned pointer (16-byte alignment required; offsets 4-byte)";
+    case FP8Q_ERR_DTYPE: return "invalid out_dtype";
+    case FP8Q_ERR_DEVICE: return "no usable HIP device";
+    case FP8Q_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t fp8q_abi_version(void) { return FP8Q_ABI_VERSION; }
+
+}  // extern "C"

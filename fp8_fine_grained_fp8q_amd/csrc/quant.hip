@@ -1,0 +1,135 @@
+// Online fine-grained E4M3 quantizers for gfx950.
+//
+// Activation tiles are 1x128 (one row, 128 consecutive K) and weight blocks 128x128, each
+// with its own FP32 scale amax/448 taken from the group's current values: codingmall.com
+// page on FP8 in DeepSeek-V3 training, sections "Dinh luong hat min" and "Dinh luong truc
+// tuyen"; risenshineclean.com DeepSeek training-algorithm page, section 3 (1x128 tile =
+// one token's 128 channels; scales computed online, no delayed scaling).
+//
+// Both kernels are HBM-bound: each reads 2 bytes and writes 1 byte per element.  Loads are
+// 16-byte per lane, so one 1x128 BF16 tile (256 B) is exactly one 16-lane DPP row and its
+// amax reduces with four row_ror steps and no LDS.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp8q_device.h"
+#include "fp8q_launch.h"
+
+namespace fp8q {
+
+// ---------------------------------------------------------------------------------------
+// Activation quantizer.  One wave handles a 16-row x 128-column slab (16 tiles): four
+// 16-byte loads per lane, lane (grp = lane/16, sub = lane%16) holding chunk `sub` of rows
+// row0 + 4*i + grp, i = 0..3.  Consecutive waves take consecutive K blocks of the same
+// rows, so a 256-thread workgroup streams 16 rows x 512 contiguous BF16 columns.  The 16
+// scales of the slab are one contiguous 64-byte run of sa[kb][.].
+// ---------------------------------------------------------------------------------------
+constexpr int kActWavesPerBlock = 4;
+
+__global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t *__restrict__ x,
+                                                              int64_t M, int64_t K,
+                                                              uint8_t *__restrict__ xq,
+                                                              float *__restrict__ sa) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = static_cast<int64_t>(blockIdx.x) * kActWavesPerBlock + (threadIdx.x >> 6);
+  const int64_t KB = K >> 7;
+  const int64_t kb = wave % KB;
+  const int64_t row0 = (wave / KB) * 16;
+  if (row0 >= M) return;
+  const int grp = lane >> 4;
+  const int sub = lane & 15;
+  const int64_t col = kb * 128 + sub * 8;
+
+  uint4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = row0 + 4 * i + grp;
+    if (row < M) {
+      v[i] = load16_stream(x + row * K + col);
+    } else {
+      v[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  float scale[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float amax = row16_max(absmax8(v[i]));
+    scale[i] = amax / kE4M3Max;  // IEEE division (correctly rounded)
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = row0 + 4 * i + grp;
+    const GroupDiv dv(scale[i]);
+    const uint2 q = quant8(v[i], dv);
+    if (row < M) *reinterpret_cast<uint2 *>(xq + row * K + col) = q;
+  }
+  // lanes sub = 0..3 of each DPP row store the scales of rows row0 + 4*sub + grp
+  if (sub < 4) {
+    const float s = sub == 0 ? scale[0] : sub == 1 ? scale[1] : sub == 2 ? scale[2] : scale[3];
+    const int64_t row = row0 + 4 * sub + grp;
+    if (row < M) sa[kb * M + row] = s;
+  }
+}
+
+hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, uint8_t *xq, float *sa,
+                            hipStream_t stream) {
+  const int64_t waves = ((M + 15) / 16) * (K / 128);
+  const int64_t blocks = (waves + kActWavesPerBlock - 1) / kActWavesPerBlock;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_act_1x128_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                     stream, x, M, K, xq, sa);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// Weight quantizer.  One 256-thread workgroup per 128x128 block: thread t holds chunk
+// t%16 of rows t/16 + 16*i, i = 0..7 (64 values in registers).  amax: DPP inside each
+// 16-lane row, readlane across the wave's four rows, LDS across the four waves.  The whole
+// block shares one scale, so the division path is uniform.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_w_128x128_kernel(const uint16_t *__restrict__ w,
+                                                              int64_t N, int64_t K,
+                                                              uint8_t *__restrict__ wq,
+                                                              float *__restrict__ sb) {
+  __shared__ float wave_max[4];
+  const int64_t KB = K >> 7, NB = N >> 7;
+  const int64_t bid = blockIdx.x;
+  const int64_t kb = bid % KB;
+  const int64_t gnb = bid / KB;  // g * NB + nb
+  const int tid = threadIdx.x;
+  const int sub = tid & 15;
+  const int r0 = tid >> 4;
+  const int64_t base = (gnb * 128) * K + kb * 128 + sub * 8;  // row gnb*128 of the [G*N][K] view
+
+  uint4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    v[i] = load16_stream(w + base + (r0 + 16 * i) * K);
+  float m = absmax8(v[0]);
+#pragma unroll
+  for (int i = 1; i < 8; ++i) m = fmaxf(m, absmax8(v[i]));
+  m = row16_max(m);
+  m = fmaxf(fmaxf(__builtin_amdgcn_readlane(m, 0), __builtin_amdgcn_readlane(m, 16)),
+            fmaxf(__builtin_amdgcn_readlane(m, 32), __builtin_amdgcn_readlane(m, 48)));
+  if ((tid & 63) == 0) wave_max[tid >> 6] = m;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+  const float s = amax / kE4M3Max;
+  const GroupDiv dv(s);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    *reinterpret_cast<uint2 *>(wq + base + (r0 + 16 * i) * K) = quant8(v[i], dv);
+  if (tid == 0) sb[gnb * KB + kb] = s;
+  (void)NB;
+}
+
+hipError_t launch_quant_w(const uint16_t *w, int64_t G, int64_t N, int64_t K, uint8_t *wq, float *sb,
+                          hipStream_t stream) {
+  const int64_t blocks = G * (N / 128) * (K / 128);
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_w_128x128_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                     stream, w, N, K, wq, sb);
+  return hipGetLastError();
+}
+
+}  // namespace fp8q

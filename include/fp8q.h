@@ -1,0 +1,136 @@
+/*
+ * fp8q.h -- C ABI of libfp8q: online fine-grained FP8 (E4M3) quantization and the
+ * block-scaled FP8 GEMM it feeds, for AMD Instinct MI355X (gfx950).
+ *
+ * What the calls compute, after the DeepSeek-V3 pages:
+ *  - dtcms.com DeepSeek-V3 page, section 3 (FP8 mixed-precision training):
+ *    3.1 the GEMMs take FP8 tensors and write BF16 or FP32; 3.2 activations are
+ *    scaled per 1x128 tile and weights per 128x128 block; 3.3 accumulation
+ *    precision is raised by promoting partial sums out of the matrix units.
+ *  - codingmall.com page on the role of FP8 precision in DeepSeek-V3 training,
+ *    sections "Dinh luong hat min" (fine-grained quantization), "Dinh luong truc
+ *    tuyen" (online quantization: every tile's / block's scale comes from its own
+ *    current maximum, no history), "Tang do chinh xac tich luy" (partial results
+ *    promoted to FP32 registers at fixed K intervals) and "Dinh dang E4M3 hop
+ *    nhat" (one format, E4M3, throughout).
+ *  - risenshineclean.com DeepSeek training-algorithm page, section 3 (the same
+ *    four points; a tile is one token's 128 channels).
+ *
+ * Numerics shared by every call (readings where the pages are silent):
+ *  - E4M3 is the OCP E4M3FN format: bias 7, largest finite 448, S.1111.111 = NaN.
+ *  - scale s = RN32(amax / 448) of the tile / block (amax = largest |x|), an FP32
+ *    value, not rounded to a power of two; all-zero groups get s = 0;
+ *  - code = E4M3(RN32(x / s)), round to nearest even, saturating, sign kept
+ *    (-0 -> 0x80); dequantized value = decode(code) * s;  FP32 subnormals kept.
+ *  - inputs are finite BF16 (NaN / Inf input: results unspecified).
+ *  - GEMM: C[m][n] = sum_kb (sa[kb][m] * sb[n/128][kb]) * P_kb[m][n], where
+ *    P_kb = sum over the 128 k of block kb of decode(xq[m][k]) * decode(wq[n][k])
+ *    is produced by FP8 matrix-core instructions and each block's P_kb is scaled
+ *    and added into an FP32 register accumulator, kb ascending (promotion every
+ *    128 K).  C = X * W^T; X is [M][K], W is [N][K], both K-contiguous.
+ *
+ * Conventions for every entry point:
+ *  - Every tensor pointer is a DEVICE pointer (hipMalloc / torch CUDA memory) on
+ *    the current HIP device; the caller owns all buffers and keeps them alive until
+ *    the work on `stream` completes.  Outputs must not alias inputs.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *    Calls are asynchronous on it and never synchronize the host.
+ *  - Arguments are checked before any HIP call; a failed check returns a negative
+ *    fp8q_status and launches nothing.  M == 0 (or M_tot == 0) is a no-op FP8Q_OK.
+ *  - Base pointers must be 16-byte aligned.  K and N must be multiples of 128.
+ *  - The library allocates no device memory and keeps no mutable global state:
+ *    calls are reentrant and thread-safe.  Kernel faults surface at the caller's
+ *    next synchronization of `stream`.
+ */
+#ifndef FP8Q_H
+#define FP8Q_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8Q_ABI_VERSION 1
+
+typedef int32_t fp8q_status;
+
+enum {
+  FP8Q_OK = 0,
+  FP8Q_ERR_NULL = -1,   /* a required pointer is NULL                                   */
+  FP8Q_ERR_SHAPE = -2,  /* negative size, K or N not a multiple of 128, G < 1, overflow */
+  FP8Q_ERR_ALIGN = -3,  /* a base pointer is not 16-byte aligned                        */
+  FP8Q_ERR_DTYPE = -4,  /* out_dtype is neither FP8Q_OUT_BF16 nor FP8Q_OUT_F32          */
+  FP8Q_ERR_DEVICE = -5, /* no usable HIP device                                          */
+  FP8Q_ERR_LAUNCH = -6  /* the kernel launch failed (hipGetLastError)                   */
+};
+
+enum { FP8Q_OUT_BF16 = 0, FP8Q_OUT_F32 = 1 };
+
+/*
+ * Activation quantizer, one scale per 1x128 tile (one row, 128 consecutive K).
+ * Source: codingmall.com FP8-in-DeepSeek-V3 page, sections "Dinh luong hat min" and
+ * "Dinh luong truc tuyen"; risenshineclean.com page, section 3 (1x128 tile = one
+ * token's 128 channels, scale computed online).
+ *   x_bf16 : [M][K] BF16 bit patterns, row-major (row stride K elements)
+ *   xq     : [M][K] E4M3 codes (out)
+ *   sa     : [K/128][M] FP32 scales (out); sa[kb][m] is the scale of row m, K block kb
+ * Requires K % 128 == 0, M >= 0.
+ */
+fp8q_status fp8q_quantize_act_1x128(const uint16_t *x_bf16, int64_t M, int64_t K, uint8_t *xq,
+                                    float *sa, void *stream);
+
+/*
+ * Weight quantizer, one scale per 128x128 block, for G stacked matrices.
+ * Source: as above (128x128 weight blocks, each scaled independently and online).
+ *   w_bf16 : [G][N][K] BF16 bit patterns, row-major
+ *   wq     : [G][N][K] E4M3 codes (out)
+ *   sb     : [G][N/128][K/128] FP32 scales (out)
+ * Requires G >= 1, N % 128 == 0, K % 128 == 0.  N == 0 is a no-op.
+ */
+fp8q_status fp8q_quantize_w_128x128(const uint16_t *w_bf16, int64_t G, int64_t N, int64_t K,
+                                    uint8_t *wq, float *sb, void *stream);
+
+/*
+ * Dense block-scaled FP8 GEMM: C = dequant(xq, sa) * dequant(wq, sb)^T.
+ * Source: dtcms.com DeepSeek-V3 page, sections 3.1 (FP8 in, BF16/FP32 out) and 3.3;
+ * codingmall.com page, section "Tang do chinh xac tich luy" (FP32 promotion at fixed
+ * K intervals; here every 128-wide K block, where the scales change).
+ *   xq [M][K] codes, sa [K/128][M] FP32  (as written by fp8q_quantize_act_1x128)
+ *   wq [N][K] codes, sb [N/128][K/128] FP32 (as written by fp8q_quantize_w_128x128, G=1)
+ *   c  [M][N] row-major, BF16 (round to nearest even) or FP32 per out_dtype (out)
+ * Requires N % 128 == 0, K % 128 == 0, K >= 128, M >= 0.
+ */
+fp8q_status fp8q_gemm_blockscaled(const uint8_t *xq, const float *sa, const uint8_t *wq,
+                                  const float *sb, int64_t M, int64_t N, int64_t K, void *c,
+                                  int32_t out_dtype, void *stream);
+
+/*
+ * Grouped (MoE expert) block-scaled FP8 GEMM.  Rows offsets[g] .. offsets[g+1]-1 of the
+ * expert-sorted activations are multiplied by expert g's weights:
+ *   C[r] = dequant(xq[r], sa[:, r]) * dequant(wq[g], sb[g])^T   for r in expert g's range.
+ * Source: as for the dense GEMM; the expert FFN GEMMs of DeepSeekMoE (8 of 256 routed
+ * experts active per token: risenshineclean.com page, section 2).
+ *   xq [M_tot][K], sa [K/128][M_tot], wq [G][N][K], sb [G][N/128][K/128]
+ *   offsets : DEVICE int32 [G+1]; must satisfy offsets[0] == 0, non-decreasing,
+ *             offsets[G] == M_tot.  Not checked on the host (that would need a sync);
+ *             the kernel clamps every range to [0, M_tot).
+ *   c [M_tot][N] (out); rows outside every expert range are left untouched.
+ * Requires G >= 1, N % 128 == 0, K % 128 == 0, K >= 128, M_tot >= 0.
+ */
+fp8q_status fp8q_grouped_gemm_blockscaled(const uint8_t *xq, const float *sa, const uint8_t *wq,
+                                          const float *sb, const int32_t *offsets, int64_t G,
+                                          int64_t M_tot, int64_t N, int64_t K, void *c,
+                                          int32_t out_dtype, void *stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *fp8q_status_string(fp8q_status status);
+
+/* FP8Q_ABI_VERSION of the built library. */
+int32_t fp8q_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8Q_H */

@@ -1,0 +1,114 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the header
+declares, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import fp8_fine_grained_fp8q_amd as fq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8q.h")
+
+ALIGNED = 1 << 20  # a fake, 16-byte aligned device address (never dereferenced)
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8q_[a-z0-9_]+)\s*\(", text)))
+
+
+def header_enums():
+    text = open(HEADER).read()
+    return {k: int(v) for k, v in re.findall(r"\b(FP8Q_[A-Z0-9_]+)\s*=\s*(-?\d+)", text)}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fq.load_library()
+
+
+def test_library_exports_every_declared_function(lib):
+    names = header_functions()
+    assert set(names) == set(fq.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", fq.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (fp8q_[a-z0-9_]+)\b", out))
+    assert set(names) <= exported
+
+
+def test_enum_values_match_binding(lib):
+    e = header_enums()
+    assert e["FP8Q_OK"] == fq.FP8Q_OK == 0
+    assert e["FP8Q_OUT_BF16"] == fq.FP8Q_OUT_BF16 and e["FP8Q_OUT_F32"] == fq.FP8Q_OUT_F32
+    assert lib.fp8q_abi_version() == fq.ABI_VERSION
+    for code in (0, -1, -2, -3, -4, -5, -6, -99):
+        assert isinstance(fq.status_string(code), str) and fq.status_string(code)
+
+
+def test_quantize_act_argument_checks(lib):
+    E = header_enums()
+    A = ALIGNED
+    assert lib.fp8q_quantize_act_1x128(A, 4, 100, A, A, None) == E["FP8Q_ERR_SHAPE"]
+    assert lib.fp8q_quantize_act_1x128(A, -1, 128, A, A, None) == E["FP8Q_ERR_SHAPE"]
+    assert lib.fp8q_quantize_act_1x128(A, 1 << 40, 1 << 30, A, A, None) == E["FP8Q_ERR_SHAPE"]
+    assert lib.fp8q_quantize_act_1x128(None, 4, 128, A, A, None) == E["FP8Q_ERR_NULL"]
+    assert lib.fp8q_quantize_act_1x128(A, 4, 128, None, A, None) == E["FP8Q_ERR_NULL"]
+    assert lib.fp8q_quantize_act_1x128(A + 2, 4, 128, A, A, None) == E["FP8Q_ERR_ALIGN"]
+    assert lib.fp8q_quantize_act_1x128(A, 4, 128, A, A + 4, None) == E["FP8Q_ERR_ALIGN"]
+    # empty work is a no-op, even with null buffers
+    assert lib.fp8q_quantize_act_1x128(None, 0, 128, None, None, None) == E["FP8Q_OK"]
+    assert lib.fp8q_quantize_act_1x128(None, 5, 0, None, None, None) == E["FP8Q_OK"]
+
+
+def test_quantize_w_argument_checks(lib):
+    E = header_enums()
+    A = ALIGNED
+    assert lib.fp8q_quantize_w_128x128(A, 0, 128, 128, A, A, None) == E["FP8Q_ERR_SHAPE"]
+    assert lib.fp8q_quantize_w_128x128(A, 1, 100, 128, A, A, None) == E["FP8Q_ERR_SHAPE"]
+    assert lib.fp8q_quantize_w_128x128(A, 1, 128, 64, A, A, None) == E["FP8Q_ERR_SHAPE"]
+    assert lib.fp8q_quantize_w_128x128(None, 1, 128, 128, A, A, None) == E["FP8Q_ERR_NULL"]
+    assert lib.fp8q_quantize_w_128x128(A, 1, 128, 128, A, A + 8, None) == E["FP8Q_ERR_ALIGN"]
+    assert lib.fp8q_quantize_w_128x128(None, 3, 0, 128, None, None, None) == E["FP8Q_OK"]
+
+
+def test_gemm_argument_checks(lib):
+    E = header_enums()
+    A = ALIGNED
+    g = lib.fp8q_gemm_blockscaled
+    assert g(A, A, A, A, 4, 128, 128, A, 7, None) == E["FP8Q_ERR_DTYPE"]
+    assert g(A, A, A, A, 4, 100, 128, A, 0, None) == E["FP8Q_ERR_SHAPE"]
+    assert g(A, A, A, A, 4, 128, 0, A, 0, None) == E["FP8Q_ERR_SHAPE"]
+    assert g(A, A, A, A, 4, 128, 200, A, 0, None) == E["FP8Q_ERR_SHAPE"]
+    assert g(A, A, A, A, -4, 128, 128, A, 0, None) == E["FP8Q_ERR_SHAPE"]
+    assert g(A, A, None, A, 4, 128, 128, A, 0, None) == E["FP8Q_ERR_NULL"]
+    assert g(A, A, A, A, 4, 128, 128, None, 0, None) == E["FP8Q_ERR_NULL"]
+    assert g(A, A, A + 1, A, 4, 128, 128, A, 0, None) == E["FP8Q_ERR_ALIGN"]
+    assert g(None, None, None, None, 0, 128, 128, None, 0, None) == E["FP8Q_OK"]
+    gg = lib.fp8q_grouped_gemm_blockscaled
+    assert gg(A, A, A, A, A, 0, 4, 128, 128, A, 0, None) == E["FP8Q_ERR_SHAPE"]
+    assert gg(A, A, A, A, None, 2, 4, 128, 128, A, 0, None) == E["FP8Q_ERR_NULL"]
+    assert gg(A, A, A, A, A + 2, 2, 4, 128, 128, A, 1, None) == E["FP8Q_ERR_ALIGN"]
+    assert gg(A, A, A, A, A, 2, 4, 128, 128, A, 3, None) == E["FP8Q_ERR_DTYPE"]
+    assert gg(None, None, None, None, None, 2, 0, 128, 128, None, 0, None) == E["FP8Q_OK"]
+
+
+def test_valid_call_without_gpu_reports_device_error(lib):
+    """On a host without a GPU a well-formed call must fail cleanly, not crash."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    E = header_enums()
+    A = ALIGNED
+    assert lib.fp8q_quantize_act_1x128(A, 4, 128, A, A, None) in (E["FP8Q_ERR_DEVICE"], E["FP8Q_ERR_LAUNCH"])
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros((4, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fq.fp8q_quantize_act_1x128(x)

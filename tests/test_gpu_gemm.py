@@ -1,0 +1,201 @@
+"""GPU parity of the block-scaled FP8 GEMMs against the oracle's FP64 dequantized product.
+
+Bar: |C_gpu - C| <= 2e-3 * ||x_hat_m||_2 * ||w_hat_n||_2 per element, C_gpu as stored
+(BF16 rounding included).  The GEMM inputs are the oracle's quantized codes and scales, so
+these tests do not depend on the GPU quantizers.  Cases: the tiny workload, ragged shapes
+spanning several 256x256 tiles with partial tails in M and N, an exactly representable
+K=128 case (bit-exact, pins the MFMA operand and output layouts), the dense 4096x7168x7168
+workload in the benchmarked launch (sampled rows and columns), grouped MoE shapes with
+empty / 1 / 127..257-row experts, the MoE up/down workloads (sampled experts), run-to-run
+determinism and untouched rows outside every expert range."""
+import numpy as np
+import pytest
+import torch
+
+import fp8_fine_grained_fp8q_amd as fq
+import workloads as wl
+from oracle import gemm as og
+from oracle import quant as oq
+
+from helpers import assert_gemm_within_tol, assert_quant_equal, dev, dev_bf16, host
+
+pytestmark = pytest.mark.gpu
+
+
+def quantized(M, N, K, seed, G=None, xscale=1.0):
+    rng = np.random.default_rng(seed)
+    x = wl.bf16_bits(rng.standard_normal((M, K), dtype=np.float32) * np.float32(xscale))
+    shape = (N, K) if G is None else (G, N, K)
+    w = wl.bf16_bits(rng.standard_normal(shape, dtype=np.float32) * np.float32(0.02))
+    return (*oq.quantize_act_1x128(x), *oq.quantize_w_128x128(w))
+
+
+def gpu_gemm(xq, sa, wq, sb, out_dtype=torch.bfloat16):
+    c = fq.fp8q_gemm_blockscaled(dev(xq), dev(sa), dev(wq), dev(sb), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return host(c).astype(np.float64)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_tiny(out_dtype):
+    c = wl.tiny()
+    xq, sa = oq.quantize_act_1x128(c["x"])
+    wq, sb = oq.quantize_w_128x128(c["w"][0])
+    ref = og.gemm_blockscaled(xq, sa, wq, sb)
+    got = gpu_gemm(xq, sa, wq, sb, out_dtype)
+    assert_gemm_within_tol(got, ref, og.row_norms_act(xq, sa), og.row_norms_w(wq, sb), "tiny")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (17, 384, 256), (255, 256, 640), (257, 640, 384),
+                                   (300, 1152, 1024), (513, 384, 128), (64, 2304, 896)])
+def test_ragged_shapes(M, N, K):
+    xq, sa, wq, sb = quantized(M, N, K, seed=M + N + K, xscale=3.0)
+    ref = og.gemm_blockscaled(xq, sa, wq, sb)
+    xn, wn = og.row_norms_act(xq, sa), og.row_norms_w(wq, sb)
+    assert_gemm_within_tol(gpu_gemm(xq, sa, wq, sb), ref, xn, wn, f"{M}x{N}x{K} bf16")
+    assert_gemm_within_tol(gpu_gemm(xq, sa, wq, sb, torch.float32), ref, xn, wn, f"{M}x{N}x{K} f32")
+
+
+def test_exact_small_integers_k128():
+    """Unit scales and small integer codes: every block partial is an exact integer in
+    FP32, so the GPU result must equal the oracle exactly.  A transposed or mis-paired
+    operand layout, or a wrong output mapping, shows up as a mismatch here."""
+    M, N, K = 48, 256, 384
+    rng = np.random.default_rng(3)
+    x = rng.integers(-8, 9, size=(M, K)).astype(np.float32)
+    w = rng.integers(-8, 9, size=(N, K)).astype(np.float32)
+    x[:, ::128] = 448.0      # every activation tile has amax 448 -> scale exactly 1
+    w[::128, ::128] = 448.0  # every weight block has amax 448 -> scale exactly 1
+    xq, sa = oq.quantize_act_1x128(wl.bf16_bits(x))
+    wq, sb = oq.quantize_w_128x128(wl.bf16_bits(w))
+    assert np.all(sa == 1.0) and np.all(sb == 1.0)
+    ref = og.gemm_blockscaled(xq, sa, wq, sb)
+    got = gpu_gemm(xq, sa, wq, sb, torch.float32)
+    bad = np.nonzero(got != ref)
+    assert bad[0].size == 0, f"{bad[0].size} mismatches, first {bad[0][0]},{bad[1][0]}: {got[bad][0]} vs {ref[bad][0]}"
+
+
+def test_deterministic():
+    xq, sa, wq, sb = quantized(300, 640, 512, seed=5)
+    a = fq.fp8q_gemm_blockscaled(dev(xq), dev(sa), dev(wq), dev(sb))
+    b = fq.fp8q_gemm_blockscaled(dev(xq), dev(sa), dev(wq), dev(sb))
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.fixture(scope="module")
+def dense_quantized():
+    c = wl.dense()
+    xq, sa = oq.quantize_act_1x128(c["x"])
+    wq, sb = oq.quantize_w_128x128(c["w"][0])
+    return xq, sa, wq, sb
+
+
+def test_dense_full_size_sampled(dense_quantized):
+    """The 4096x7168x7168 workload in the benchmarked launch; every output checked against
+    the oracle on 48 random rows (all columns) and 48 random columns (all rows)."""
+    xq, sa, wq, sb = dense_quantized
+    got = gpu_gemm(xq, sa, wq, sb)
+    M, N = got.shape
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(M, 48, replace=False))
+    cols = np.sort(rng.choice(N, 48, replace=False))
+    wh = oq.dequant_w(wq, sb)
+    xr = oq.dequant_act(xq[rows], np.ascontiguousarray(sa[:, rows]))
+    ref_rows = xr @ wh.T
+    xn_all = og.row_norms_act(xq, sa)
+    wn_all = np.linalg.norm(wh, axis=1)
+    assert_gemm_within_tol(got[rows], ref_rows, xn_all[rows], wn_all, "dense rows")
+    xh = oq.dequant_act(xq, sa)
+    ref_cols = xh @ wh[cols].T
+    assert_gemm_within_tol(got[:, cols], ref_cols, xn_all, wn_all[cols], "dense cols")
+
+
+def run_grouped(xq, sa, wq, sb, offsets, out_dtype=torch.bfloat16, fill=None):
+    M, N = xq.shape[0], wq.shape[1]
+    out = None
+    if fill is not None:
+        out = torch.full((M, N), fill, dtype=out_dtype, device="cuda")
+    c = fq.fp8q_grouped_gemm_blockscaled(dev(xq), dev(sa), dev(wq), dev(sb), dev(offsets),
+                                         out_dtype=out_dtype, out=out)
+    torch.cuda.synchronize()
+    return host(c).astype(np.float64)
+
+
+@pytest.mark.parametrize("sizes", [[0, 1, 127, 128, 129, 255, 256, 257], [300], [0, 0, 5, 0],
+                                   [513, 2, 0, 260]])
+def test_grouped_edge_sizes(sizes):
+    G, N, K = len(sizes), 384, 256
+    offsets = np.zeros(G + 1, np.int32)
+    offsets[1:] = np.cumsum(sizes)
+    M = int(offsets[-1])
+    xq, sa, wq, sb = quantized(M, N, K, seed=sum(sizes) + G, G=G, xscale=2.0)
+    ref = og.grouped_gemm_blockscaled(xq, sa, wq, sb, offsets)
+    got = run_grouped(xq, sa, wq, sb, offsets)
+    xn = og.row_norms_act(xq, sa)
+    for g in range(G):
+        lo, hi = offsets[g], offsets[g + 1]
+        if hi > lo:
+            wn = og.row_norms_w(wq[g], sb[g])
+            assert_gemm_within_tol(got[lo:hi], ref[lo:hi], xn[lo:hi], wn, f"expert {g} ({hi - lo} rows)")
+
+
+def test_grouped_single_expert_equals_dense():
+    xq, sa, wq, sb = quantized(300, 640, 384, seed=21)
+    dense = gpu_gemm(xq, sa, wq, sb)
+    grouped = run_grouped(xq, sa, wq[None], sb[None], np.array([0, 300], np.int32))
+    assert np.array_equal(dense, grouped)
+
+
+def test_grouped_rows_outside_ranges_untouched():
+    """offsets[G] < M_tot: the trailing rows belong to no expert and keep their contents."""
+    G, N, K = 2, 256, 256
+    xq, sa, wq, sb = quantized(200, N, K, seed=8, G=G)
+    offsets = np.array([0, 70, 150], np.int32)
+    got = run_grouped(xq, sa, wq, sb, offsets, out_dtype=torch.float32, fill=-777.0)
+    assert np.all(got[150:] == -777.0)
+    ref = og.grouped_gemm_blockscaled(xq, sa, wq, sb, offsets)
+    xn = og.row_norms_act(xq, sa)
+    for g in range(G):
+        lo, hi = offsets[g], offsets[g + 1]
+        assert_gemm_within_tol(got[lo:hi], ref[lo:hi], xn[lo:hi], og.row_norms_w(wq[g], sb[g]), f"expert {g}")
+
+
+@pytest.mark.parametrize("name", ["moe_up", "moe_down"])
+def test_moe_workloads_sampled(name):
+    """Full-size MoE workloads (32 local experts, routed token counts).  Four experts (first,
+    two middle, last non-empty) are checked row by row against the oracle.  Their GEMM
+    inputs are the oracle's codes and scales; the other experts' inputs come from the GPU
+    quantizers (their outputs are not checked), and for the sampled experts the GPU
+    quantizers' output must equal the oracle's bit for bit."""
+    c = wl.CONFIGS[name]()
+    offsets = c["offsets"]
+    x_d = dev_bf16(c["x"])
+    w_d = dev_bf16(c["w"])
+    xq_d, sa_d = fq.fp8q_quantize_act_1x128(x_d)
+    wq_d, sb_d = fq.fp8q_quantize_w_128x128(w_d)
+    torch.cuda.synchronize()
+    nz = [g for g in range(len(offsets) - 1) if offsets[g + 1] > offsets[g]]
+    pick = sorted(set([nz[0], nz[len(nz) // 3], nz[2 * len(nz) // 3], nz[-1]]))
+    ref_in = {}
+    for g in pick:
+        lo, hi = int(offsets[g]), int(offsets[g + 1])
+        xq_g, sa_g = oq.quantize_act_1x128(c["x"][lo:hi])
+        wq_g, sb_g = oq.quantize_w_128x128(c["w"][g])
+        assert_quant_equal(xq_d[lo:hi], sa_d[:, lo:hi].contiguous(), xq_g, sa_g, f"{name} act rows of expert {g}")
+        assert_quant_equal(wq_d[g], sb_d[g], wq_g, sb_g, f"{name} weights of expert {g}")
+        xq_d[lo:hi] = dev(xq_g)
+        sa_d[:, lo:hi] = dev(sa_g)
+        wq_d[g] = dev(wq_g)
+        sb_d[g] = dev(sb_g)
+        ref_in[g] = (xq_g, sa_g, wq_g, sb_g)
+    out = fq.fp8q_grouped_gemm_blockscaled(xq_d, sa_d, wq_d, sb_d, dev(offsets))
+    torch.cuda.synchronize()
+    got = host(out).astype(np.float64)
+    for g in pick:
+        lo, hi = int(offsets[g]), int(offsets[g + 1])
+        xq_g, sa_g, wq_g, sb_g = ref_in[g]
+        xh = oq.dequant_act(xq_g, sa_g)
+        wh = oq.dequant_w(wq_g, sb_g)
+        assert_gemm_within_tol(got[lo:hi], xh @ wh.T, np.linalg.norm(xh, axis=1),
+                               np.linalg.norm(wh, axis=1), f"{name} expert {g}")
