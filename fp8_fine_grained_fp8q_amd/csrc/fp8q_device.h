@@ -23,6 +23,11 @@ __device__ __forceinline__ uint4 load16_stream(const void *p) {
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
+// Lane `src` of a float held in every lane (readlane is an integer builtin: pass the bits).
+__device__ __forceinline__ float lane_f32(float v, int src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src));
+}
+
 // Maximum over the 16 lanes of a DPP row (lanes 16r .. 16r+15), left in every lane of the
 // row.  Four rotate-and-max steps (row_ror 8, 4, 2, 1) stay inside the row.
 __device__ __forceinline__ float row16_max(float v) {
@@ -62,14 +67,16 @@ struct GroupDiv {
       mode = 2;
     }
   }
-  // The correctly rounded fast-path quotient (valid for mode 1 only).
+  // The correctly rounded fast-path quotient (valid for mode 1 only).  The corrections
+  // can turn a zero quotient's sign positive (-0 - (+0) = +0), so the sign of x is put
+  // back; the quotient of x by a positive scale always has the sign of x.
   __device__ __forceinline__ float fast(float x) const {
 #pragma clang fp contract(off)
     const float q0 = x * r;
     const float e1 = __builtin_fmaf(-q0, s, x);
     const float y1 = __builtin_fmaf(e1, r, q0);
     const float e2 = __builtin_fmaf(-y1, s, x);
-    return __builtin_fmaf(e2, r, y1);
+    return __builtin_copysignf(__builtin_fmaf(e2, r, y1), x);
   }
 };
 

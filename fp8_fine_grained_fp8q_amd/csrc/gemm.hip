@@ -226,7 +226,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(
   // repeats that block), so the promotion FMAs stay next to their MFMAs.
   auto step = [&](const FP8Q_LDS uint8_t *cx, const FP8Q_LDS uint8_t *cw, FP8Q_LDS uint8_t *nx,
                   FP8Q_LDS uint8_t *nw, int kb) {
-    __syncthreads();  // stage kb has landed; every wave is done with the other buffer
+    // Stage kb has landed in LDS once every wave's own copies are done (vmcnt(0) before
+    // the barrier: the compiler's fence does not count direct-to-LDS loads), and after
+    // the barrier every wave is also done reading the other buffer.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
     const int kn = kb + 1 < KB ? kb + 1 : kb;
     const uint32_t koff = static_cast<uint32_t>(kn) * kBK;
     stage_load(rx, off, koff, nx, wave);
@@ -263,7 +267,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(
     step(lx1, lw1, lx0, lw0, kb + 1);
   }
   if (kb < KB) step(lx0, lw0, lx1, lw1, kb);
-  __syncthreads();  // the last (repeated) copy is drained before the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the last (repeated) copy
 
   // Epilogue: lane owns row m = m_begin + wm*64 + f*16 + l16 and columns
   // n0 + wn*128 + j*16 + 4*kg + {0..3}.

@@ -109,8 +109,7 @@ __global__ __launch_bounds__(256) void quant_w_128x128_kernel(const uint16_t *__
 #pragma unroll
   for (int i = 1; i < 8; ++i) m = fmaxf(m, absmax8(v[i]));
   m = row16_max(m);
-  m = fmaxf(fmaxf(__builtin_amdgcn_readlane(m, 0), __builtin_amdgcn_readlane(m, 16)),
-            fmaxf(__builtin_amdgcn_readlane(m, 32), __builtin_amdgcn_readlane(m, 48)));
+  m = fmaxf(fmaxf(lane_f32(m, 0), lane_f32(m, 16)), fmaxf(lane_f32(m, 32), lane_f32(m, 48)));
   if ((tid & 63) == 0) wave_max[tid >> 6] = m;
   __syncthreads();
   const float amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));

@@ -47,4 +47,6 @@ def assert_gemm_within_tol(c_gpu: np.ndarray, c_ref: np.ndarray, xnorm, wnorm, w
     worst = np.unravel_index(np.argmax(err / np.maximum(tol, 1e-300)), err.shape)
     assert np.all(err <= tol), (f"{what}: {np.count_nonzero(err > tol)} elements out of tolerance; "
                                 f"worst at {worst}: gpu {c_gpu[worst]} ref {c_ref[worst]} tol {tol[worst]}")
-    return float(np.max(err / np.maximum(tol, 1e-300)))
+    ratio = float(np.max(err / np.maximum(tol, 1e-300)))
+    print(f"[{what}] max |err|/tol = {ratio:.4f}", flush=True)
+    return ratio

@@ -4,8 +4,9 @@ Bar: |C_gpu - C| <= 2e-3 * ||x_hat_m||_2 * ||w_hat_n||_2 per element, C_gpu as s
 (BF16 rounding included).  The GEMM inputs are the oracle's quantized codes and scales, so
 these tests do not depend on the GPU quantizers.  Cases: the tiny workload, ragged shapes
 spanning several 256x256 tiles with partial tails in M and N, an exactly representable
-K=128 case (bit-exact, pins the MFMA operand and output layouts), the dense 4096x7168x7168
-workload in the benchmarked launch (sampled rows and columns), grouped MoE shapes with
+integer case (bit-exact, pins the MFMA operand and output layouts), a characterisation of
+the matrix core's own block summation, the dense 4096x7168x7168
+workload in the benchmarked launch (every output), grouped MoE shapes with
 empty / 1 / 127..257-row experts, the MoE up/down workloads (sampled experts), run-to-run
 determinism and untouched rows outside every expert range."""
 import numpy as np
@@ -56,16 +57,20 @@ def test_ragged_shapes(M, N, K):
     assert_gemm_within_tol(gpu_gemm(xq, sa, wq, sb, torch.float32), ref, xn, wn, f"{M}x{N}x{K} f32")
 
 
-def test_exact_small_integers_k128():
-    """Unit scales and small integer codes: every block partial is an exact integer in
-    FP32, so the GPU result must equal the oracle exactly.  A transposed or mis-paired
-    operand layout, or a wrong output mapping, shows up as a mismatch here."""
+def test_exact_small_integers():
+    """Unit scales and small integer codes whose products all lie in [-64, 64]: every
+    block partial is an integer far inside FP32's exact range and inside the matrix core's
+    exact range, so the GPU result must equal the oracle exactly.  A transposed or
+    mis-paired operand layout, or a wrong output mapping, shows up as a mismatch here.
+    The 448 entries that pin every scale to 1 are placed where they only meet zeros."""
     M, N, K = 48, 256, 384
     rng = np.random.default_rng(3)
     x = rng.integers(-8, 9, size=(M, K)).astype(np.float32)
     w = rng.integers(-8, 9, size=(N, K)).astype(np.float32)
-    x[:, ::128] = 448.0      # every activation tile has amax 448 -> scale exactly 1
-    w[::128, ::128] = 448.0  # every weight block has amax 448 -> scale exactly 1
+    x[:, ::128] = 448.0          # activation tile amax -> scale 1
+    w[:, ::128] = 0.0            # ... meets only zeros
+    w[127::128, 127::128] = 448.0  # weight block amax -> scale 1
+    x[:, 127::128] = 0.0         # ... meets only zeros
     xq, sa = oq.quantize_act_1x128(wl.bf16_bits(x))
     wq, sb = oq.quantize_w_128x128(wl.bf16_bits(w))
     assert np.all(sa == 1.0) and np.all(sb == 1.0)
@@ -73,6 +78,32 @@ def test_exact_small_integers_k128():
     got = gpu_gemm(xq, sa, wq, sb, torch.float32)
     bad = np.nonzero(got != ref)
     assert bad[0].size == 0, f"{bad[0].size} mismatches, first {bad[0][0]},{bad[1][0]}: {got[bad][0]} vs {ref[bad][0]}"
+
+
+def test_block_partial_precision_with_a_dominant_product():
+    """Characterises the FP8 matrix core's own summation of one block's 128 products:
+    each block holds one product 448*448 = 200704 and 127 products of magnitude <= 64
+    (unit scales, so the exact result is an integer well inside FP32's exact range).  The
+    hardware's sum is not exact in this case (the small products lose low-order bits
+    against the large one), which is the accumulation-precision limit the promotion scheme
+    is about; the result must still meet the acceptance bound.  Prints the observed error."""
+    M, N, K = 48, 256, 384
+    rng = np.random.default_rng(3)
+    x = rng.integers(-8, 9, size=(M, K)).astype(np.float32)
+    w = rng.integers(-8, 9, size=(N, K)).astype(np.float32)
+    x[:, ::128] = 448.0
+    w[::128, ::128] = 448.0
+    xq, sa = oq.quantize_act_1x128(wl.bf16_bits(x))
+    wq, sb = oq.quantize_w_128x128(wl.bf16_bits(w))
+    assert np.all(sa == 1.0) and np.all(sb == 1.0)
+    ref = og.gemm_blockscaled(xq, sa, wq, sb)
+    got = gpu_gemm(xq, sa, wq, sb, torch.float32)
+    dom = np.zeros(N, bool)
+    dom[::128] = True
+    err = np.abs(got - ref)
+    print(f"\n[block-partial precision] rows with a 200704 product per block: max |err| "
+          f"{err[:, dom].max():g} (of |C| ~ {np.abs(ref[:, dom]).max():g}); other rows max |err| {err[:, ~dom].max():g}")
+    assert_gemm_within_tol(got, ref, og.row_norms_act(xq, sa), og.row_norms_w(wq, sb), "dominant product")
 
 
 def test_deterministic():
@@ -91,24 +122,26 @@ def dense_quantized():
     return xq, sa, wq, sb
 
 
-def test_dense_full_size_sampled(dense_quantized):
-    """The 4096x7168x7168 workload in the benchmarked launch; every output checked against
-    the oracle on 48 random rows (all columns) and 48 random columns (all rows)."""
+def test_dense_full_size(dense_quantized):
+    """The 4096x7168x7168 workload in the benchmarked launch, every output checked against
+    the oracle (an FP64 product of the dequantized operands: a few seconds on the host)."""
     xq, sa, wq, sb = dense_quantized
     got = gpu_gemm(xq, sa, wq, sb)
-    M, N = got.shape
-    rng = np.random.default_rng(0)
-    rows = np.sort(rng.choice(M, 48, replace=False))
-    cols = np.sort(rng.choice(N, 48, replace=False))
-    wh = oq.dequant_w(wq, sb)
-    xr = oq.dequant_act(xq[rows], np.ascontiguousarray(sa[:, rows]))
-    ref_rows = xr @ wh.T
-    xn_all = og.row_norms_act(xq, sa)
-    wn_all = np.linalg.norm(wh, axis=1)
-    assert_gemm_within_tol(got[rows], ref_rows, xn_all[rows], wn_all, "dense rows")
     xh = oq.dequant_act(xq, sa)
-    ref_cols = xh @ wh[cols].T
-    assert_gemm_within_tol(got[:, cols], ref_cols, xn_all, wn_all[cols], "dense cols")
+    wh = oq.dequant_w(wq, sb)
+    ref = xh @ wh.T
+    assert_gemm_within_tol(got, ref, np.linalg.norm(xh, axis=1), np.linalg.norm(wh, axis=1), "dense 4096x7168x7168")
+
+
+def test_dense_full_size_repeatable(dense_quantized):
+    """Ten launches at full size give bit-identical output (no cross-wave races in the
+    LDS pipeline; the kernel has no atomics or split reductions)."""
+    xq, sa, wq, sb = (dev(a) for a in dense_quantized)
+    first = fq.fp8q_gemm_blockscaled(xq, sa, wq, sb)
+    for _ in range(9):
+        again = fq.fp8q_gemm_blockscaled(xq, sa, wq, sb)
+        torch.cuda.synchronize()
+        assert torch.equal(first.view(torch.int16), again.view(torch.int16))
 
 
 def run_grouped(xq, sa, wq, sb, offsets, out_dtype=torch.bfloat16, fill=None):
@@ -189,8 +222,12 @@ def test_moe_workloads_sampled(name):
         wq_d[g] = dev(wq_g)
         sb_d[g] = dev(sb_g)
         ref_in[g] = (xq_g, sa_g, wq_g, sb_g)
-    out = fq.fp8q_grouped_gemm_blockscaled(xq_d, sa_d, wq_d, sb_d, dev(offsets))
-    torch.cuda.synchronize()
+    off_d = dev(offsets)
+    out = fq.fp8q_grouped_gemm_blockscaled(xq_d, sa_d, wq_d, sb_d, off_d)
+    for _ in range(3):  # repeatable at full size
+        again = fq.fp8q_grouped_gemm_blockscaled(xq_d, sa_d, wq_d, sb_d, off_d)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), again.view(torch.int16))
     got = host(out).astype(np.float64)
     for g in pick:
         lo, hi = int(offsets[g]), int(offsets[g + 1])
