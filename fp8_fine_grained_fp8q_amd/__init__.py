@@ -22,7 +22,8 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libfp8q.so")
+# FP8Q_LIBRARY may point at another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("FP8Q_LIBRARY") or os.path.join(HERE, "libfp8q.so")
 
 FP8Q_OK = 0
 FP8Q_OUT_BF16 = 0

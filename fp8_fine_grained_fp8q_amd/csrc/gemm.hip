@@ -10,22 +10,23 @@
 // training-algorithm page, section 3, "accumulation precision").  On gfx950 one
 // v_mfma_f32_16x16x128_f8f6f4 covers exactly one 128-wide K block of a 16x16 output tile,
 // so each MFMA result is a complete block partial P_kb: it starts from C = 0 and is folded
-// into the FP32 accumulator with one FMA per element, acc = P * (sa*sb) + acc.  That FMA
-// runs on the vector ALU while the matrix core works on the next MFMA.
+// into the FP32 accumulator with one FMA per element, acc = P * (sa*sb) + acc.  Those FMAs
+// run on the vector ALU one fragment column behind the MFMAs, so the matrix core is never
+// waiting on them.
 //
-// Workgroup tile 256(M) x 256(N), K step 128 (= the scale block), 8 waves in a 4(M) x 2(N)
-// grid, each owning 64 x 128 outputs (128 FP32 accumulator VGPRs).  The MFMA takes the
-// weight fragment as its A operand and the activation fragment as B, so every lane owns
-// one output row m and four consecutive columns n: one activation scale per fragment row
-// and 8- or 16-byte output stores.
+// Workgroup tile 256(M) x BN(N) with BN = 32*NFR (256 or 224, picked per shape so that the
+// tiles fill the GPU in whole rounds), K step 128 (= the scale block), 8 waves in a 4(M) x
+// 2(N) grid, each owning 64 x 16*NFR outputs (4*NFR*4 FP32 accumulator VGPRs).  The MFMA
+// takes the weight fragment as its A operand and the activation fragment as B, so every
+// lane owns one output row m and four consecutive columns n: one activation scale per
+// fragment row and 8- or 16-byte output stores.
 //
-// Operand staging: both 256x128-byte stages live in LDS, double buffered (4 x 32 KB).
-// gfx950's global_load_lds_dwordx4 moves 16 B per lane straight from global memory into
-// LDS; each wave's load fills 1 KB = 8 rows.  The lane->address map applies an XOR swizzle
-// of the 16-byte chunk index with the row (row & 7) so that the fragment reads
-// (ds_read_b128, 16 rows of one chunk column) hit distinct banks.  The two buffers are
-// separate LDS arrays, so the compiler can see that reading one does not wait for the
-// loads in flight into the other.
+// Operand staging: both stages live in LDS, double buffered.  gfx950's buffer_load ... lds
+// moves 16 B per lane from global memory straight into LDS; each wave's load fills 1 KB =
+// 8 rows of 128 B.  The lane->address map applies an XOR swizzle of the 16-byte chunk
+// index with the row so the fragment reads (ds_read_b128, 16 consecutive rows of one chunk
+// column) spread over the banks.  The two buffers are separate LDS arrays, so the compiler
+// can see that reading one does not wait for the loads in flight into the other.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -39,13 +40,20 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 #define FP8Q_LDS __attribute__((address_space(3)))
 
 constexpr int kBM = 256;
-constexpr int kBN = 256;
 constexpr int kBK = 128;
 constexpr int kThreads = 512;
-constexpr int kStage = kBM * kBK;  // bytes of one operand stage (kBM == kBN)
-constexpr int kGroupM = 8;         // M tiles per raster group (L2 reuse of weight panels)
+constexpr int kGroupM = 8;  // M tiles per raster group (L2 reuse of weight panels)
 
-__device__ __forceinline__ int swz(int row) { return row & 7; }
+#ifndef FP8Q_JBARRIER
+#define FP8Q_JBARRIER 1
+#endif
+#ifndef FP8Q_SWZ_MODE
+#define FP8Q_SWZ_MODE 1
+#endif
+// XOR swizzle of the 16-byte chunk index by row.  Mode 1 spreads rows 2i and 2i+1 over
+// the two 128-byte halves of a 256-byte bank line and pairs i over the 8 chunk slots
+// (conflict-free for 16 lanes with 64 banks of 4 bytes); mode 0 separates 8 rows.
+__device__ __forceinline__ int swz(int row) { return FP8Q_SWZ_MODE ? ((row >> 1) & 7) : (row & 7); }
 
 // Buffer resource (gfx9 family layout) over `bytes` bytes at `p`; loads at or past the
 // end return zeros, which is how rows beyond the tile's valid range are filled.
@@ -54,10 +62,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
                                            static_cast<int>(bytes), 0x00020000);
 }
 
-// Per-lane byte offsets of the four 16-byte pieces a lane moves for one 256-row x 128-byte
-// stage: wave w fills LDS chunks c = 8*i + w (8 rows each, 1 KB); lane p of chunk c lands
-// at LDS row 8c + p/8, slot p%8, and fetches global chunk slot ^ swz(row) of that row.
-// The same offsets serve both operands (both tiles are 256 rows with row stride K).
+// Per-lane byte offsets of the pieces a lane moves for one stage: wave w fills LDS chunks
+// c = 8*i + w (8 rows each, 1 KB); lane p of chunk c lands at LDS row 8c + p/8, slot p%8,
+// and fetches global chunk slot ^ swz(row) of that row.  Both operands use these offsets
+// (both have row stride K).
 __device__ __forceinline__ void stage_offsets(int64_t K, int wave, int lane, uint32_t off[4]) {
   const int r_in = lane >> 3;
   const int slot = lane & 7;
@@ -68,7 +76,10 @@ __device__ __forceinline__ void stage_offsets(int64_t K, int wave, int lane, uin
   }
 }
 
-// Copy one stage (K bytes [koff, koff + 128) of all 256 tile rows) into LDS.
+// Copy one stage (K bytes [koff, koff + 128) of 256 operand rows) into LDS.  Rows past
+// the resource's end (a 224-row weight tile, a ragged edge) are filled with zeros by the
+// buffer bounds check without touching memory, so every wave always issues four loads and
+// the loop body stays free of branches.
 __device__ __forceinline__ void stage_load(__amdgpu_buffer_rsrc_t rsrc, const uint32_t off[4], uint32_t koff,
                                            FP8Q_LDS uint8_t *lds, int wave) {
 #pragma unroll
@@ -99,8 +110,8 @@ struct Tile {
   const float *sb;  // its block scales, [N/128][K/128]
 };
 
-__device__ __forceinline__ bool dense_tile(int64_t M, int64_t N, const uint8_t *wq, const float *sb,
-                                           Tile &t) {
+template <int kBN>
+__device__ __forceinline__ void dense_tile(int64_t M, int64_t N, const uint8_t *wq, const float *sb, Tile &t) {
   const int tiles_m = static_cast<int>((M + kBM - 1) / kBM);
   const int tiles_n = static_cast<int>((N + kBN - 1) / kBN);
   const int total = tiles_m * tiles_n;
@@ -123,25 +134,24 @@ __device__ __forceinline__ bool dense_tile(int64_t M, int64_t N, const uint8_t *
   t.n0 = static_cast<int64_t>(tn) * kBN;
   t.w = wq;
   t.sb = sb;
-  return true;
 }
 
 // Grouped: blockIdx.y is the N tile, blockIdx.x enumerates the M tiles of all experts in
 // order (expert g contributes ceil(n_g / 256) tiles).  Offsets come from device memory;
 // every range is clamped to [0, M_tot).
+template <int kBN>
 __device__ __forceinline__ bool grouped_tile(const int32_t *__restrict__ offsets, int G, int64_t M_tot,
                                              int64_t N, int64_t K, const uint8_t *wq, const float *sb,
                                              Tile &t) {
   const int slot = blockIdx.x;
   int cum = 0;
-  int64_t lo = 0;
   for (int g = 0; g < G; ++g) {
     int64_t a = offsets[g], b = offsets[g + 1];
     a = a < 0 ? 0 : (a > M_tot ? M_tot : a);
     b = b < a ? a : (b > M_tot ? M_tot : b);
     const int tiles = static_cast<int>((b - a + kBM - 1) / kBM);
     if (slot < cum + tiles) {
-      lo = a + static_cast<int64_t>(slot - cum) * kBM;
+      const int64_t lo = a + static_cast<int64_t>(slot - cum) * kBM;
       t.m_begin = lo;
       t.rows = static_cast<int>(min(static_cast<int64_t>(kBM), b - lo));
       t.n0 = static_cast<int64_t>(blockIdx.y) * kBN;
@@ -154,28 +164,31 @@ __device__ __forceinline__ bool grouped_tile(const int32_t *__restrict__ offsets
   return false;
 }
 
-template <bool kGrouped>
+template <int NFR, bool kGrouped>
 __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(
     const uint8_t *__restrict__ xq, const float *__restrict__ sa, const uint8_t *__restrict__ wq,
     const float *__restrict__ sb, const int32_t *__restrict__ offsets, int G, int64_t M, int64_t N,
     int64_t K, void *__restrict__ c, int out_f32) {
-  __shared__ __attribute__((aligned(1024))) uint8_t sx0[kStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t sw0[kStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t sx1[kStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t sw1[kStage];
+  constexpr int kBN = 32 * NFR;      // tile columns
+  constexpr int kWN = 16 * NFR;      // columns per wave
+  // Both operand stages hold 256 rows; a 224-column tile leaves the last 32 W rows zero.
+  __shared__ __attribute__((aligned(1024))) uint8_t sx0[kBM * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t sw0[kBM * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t sx1[kBM * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t sw1[kBM * kBK];
 
   Tile t;
   if (kGrouped) {
-    if (!grouped_tile(offsets, G, M, N, K, wq, sb, t)) return;
+    if (!grouped_tile<kBN>(offsets, G, M, N, K, wq, sb, t)) return;
   } else {
-    dense_tile(M, N, wq, sb, t);
+    dense_tile<kBN>(M, N, wq, sb, t);
   }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1;  // 0..3: rows wm*64 .. +63
-  const int wn = wave & 1;   // 0..1: cols wn*128 .. +127
+  const int wn = wave & 1;   // 0..1: cols wn*kWN .. +kWN-1
   const int KB = static_cast<int>(K >> 7);
   const int NB = static_cast<int>(N >> 7);
   const int l16 = lane & 15;
@@ -195,18 +208,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(
     const int r = wm * 64 + f * 16 + l16;
     srow[f] = static_cast<int>(t.m_begin) + (r < t.rows ? r : t.rows - 1);
   }
-  int nb = static_cast<int>((t.n0 + wn * 128) >> 7);  // this wave's 128-column block
-  if (nb > NB - 1) nb = NB - 1;
-  const float *sbrow = t.sb + static_cast<int64_t>(nb) * KB;
+  // Weight-block scales: the wave's columns start in 128-column block nb0; fragment
+  // columns j >= jsplit lie in block nb0 + 1 (only possible when kWN is not 128).
+  const int64_t wc0 = t.n0 + wn * kWN;
+  const int nb0 = static_cast<int>(min(static_cast<int64_t>(NB - 1), wc0 >> 7));
+  const int nb1 = min(NB - 1, nb0 + 1);
+  const int jsplit = NFR == 8 ? 8 : static_cast<int>((128 - (wc0 & 127)) >> 4);
+  const float *sbrow0 = t.sb + static_cast<int64_t>(nb0) * KB;
+  const float *sbrow1 = t.sb + static_cast<int64_t>(nb1) * KB;
 
-  v4f acc[4][8];
+  v4f acc[4][NFR];
 #pragma unroll
   for (int f = 0; f < 4; ++f)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[f][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < NFR; ++j) acc[f][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   float sa_cur[4], sa_nxt[4];
-  float sb_cur, sb_nxt = 0.0f;
+  float sb0_cur, sb1_cur, sb0_nxt = 0.0f, sb1_nxt = 0.0f;
 
   FP8Q_LDS uint8_t *lx0 = (FP8Q_LDS uint8_t *)sx0;
   FP8Q_LDS uint8_t *lw0 = (FP8Q_LDS uint8_t *)sw0;
@@ -216,14 +234,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(
   stage_load(rw, off, 0, lw0, wave);
 #pragma unroll
   for (int f = 0; f < 4; ++f) sa_cur[f] = sa[srow[f]];
-  sb_cur = sbrow[0];
+  sb0_cur = sbrow0[0];
+  sb1_cur = sbrow1[0];
 #pragma unroll
   for (int f = 0; f < 4; ++f) sa_nxt[f] = 0.0f;
 
   // One K block: wait for its stage, start the copy of the next one into the other
-  // buffer, then 32 MFMAs (one per 16x16 fragment pair) each folded into the FP32
-  // accumulator with its scale.  The body is branch-free (at the last block the copy just
-  // repeats that block), so the promotion FMAs stay next to their MFMAs.
+  // buffer, then 4*NFR MFMAs (one per 16x16 fragment pair).  The promotion is software
+  // pipelined: the block partials of fragment column j are folded into the accumulator
+  // (one FMA per element with that row's scale sa*sb) while the MFMAs of column j+1 run;
+  // the last column's partials are folded during the next block's first column.  The
+  // body is branch-free (at the last block the copy just repeats that block).
+  v4f pp[4];      // partials waiting to be folded
+  float sclp[4];  // scales of the previous block's last column
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    pp[f] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    sclp[f] = 0.0f;
+  }
   auto step = [&](const FP8Q_LDS uint8_t *cx, const FP8Q_LDS uint8_t *cw, FP8Q_LDS uint8_t *nx,
                   FP8Q_LDS uint8_t *nw, int kb) {
     // Stage kb has landed in LDS once every wave's own copies are done (vmcnt(0) before
@@ -231,6 +259,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(
     // the barrier every wave is also done reading the other buffer.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    // Operands of the first MFMA first, then the copies of the next stage, then the other
+    // activation fragments.
+    v8i wnext = frag(cw, wn * kWN + l16, kg);
+    v8i xf[4];
+    xf[0] = frag(cx, wm * 64 + l16, kg);
     const int kn = kb + 1 < KB ? kb + 1 : kb;
     const uint32_t koff = static_cast<uint32_t>(kn) * kBK;
     stage_load(rx, off, koff, nx, wave);
@@ -238,27 +271,38 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(
     const float *sak = sa + static_cast<int64_t>(kn) * M;
 #pragma unroll
     for (int f = 0; f < 4; ++f) sa_nxt[f] = sak[srow[f]];
-    sb_nxt = sbrow[kn];
-    float scl[4];
+    sb0_nxt = sbrow0[kn];
+    sb1_nxt = sbrow1[kn];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) scl[f] = sa_cur[f] * sb_cur;
-    v8i xf[4];
+    for (int f = 1; f < 4; ++f) xf[f] = frag(cx, wm * 64 + f * 16 + l16, kg);
 #pragma unroll
-    for (int f = 0; f < 4; ++f) xf[f] = frag(cx, wm * 64 + f * 16 + l16, kg);
+    for (int j = 0; j < NFR; ++j) {
+      const v8i wf = wnext;
+      if (j + 1 < NFR) wnext = frag(cw, wn * kWN + (j + 1) * 16 + l16, kg);
+      v4f np[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const v8i wf = frag(cw, wn * 128 + j * 16 + l16, kg);
+      for (int f = 0; f < 4; ++f) np[f] = mfma_block(wf, xf[f]);
+      const int jp = j == 0 ? NFR - 1 : j - 1;
+      const float sbj = jp < jsplit ? sb0_cur : sb1_cur;  // wave-uniform
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
-        const v4f p = mfma_block(wf, xf[f]);
+        const float sc = j == 0 ? sclp[f] : sa_cur[f] * sbj;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[f][j][i] = __builtin_fmaf(p[i], scl[f], acc[f][j][i]);
-        asm volatile("" : "+v"(acc[f][j]));  // keep the promotion here, not sunk later
+        for (int i = 0; i < 4; ++i) acc[f][jp][i] = __builtin_fmaf(pp[f][i], sc, acc[f][jp][i]);
+        pp[f] = np[f];
       }
+#if FP8Q_JBARRIER
+      __builtin_amdgcn_sched_barrier(0);
+#endif
     }
+    const float sbl = NFR - 1 < jsplit ? sb0_cur : sb1_cur;
 #pragma unroll
-    for (int f = 0; f < 4; ++f) sa_cur[f] = sa_nxt[f];
-    sb_cur = sb_nxt;
+    for (int f = 0; f < 4; ++f) {
+      sclp[f] = sa_cur[f] * sbl;
+      sa_cur[f] = sa_nxt[f];
+    }
+    sb0_cur = sb0_nxt;
+    sb1_cur = sb1_nxt;
   };
 
   int kb = 0;
@@ -268,17 +312,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(
   }
   if (kb < KB) step(lx0, lw0, lx1, lw1, kb);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the last (repeated) copy
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[f][NFR - 1][i] = __builtin_fmaf(pp[f][i], sclp[f], acc[f][NFR - 1][i]);
 
   // Epilogue: lane owns row m = m_begin + wm*64 + f*16 + l16 and columns
-  // n0 + wn*128 + j*16 + 4*kg + {0..3}.
+  // n0 + wn*kWN + j*16 + 4*kg + {0..3}.
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
     const int r = wm * 64 + f * 16 + l16;
     if (r >= t.rows) continue;
     const int64_t m = t.m_begin + r;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t n = t.n0 + wn * 128 + j * 16 + 4 * kg;
+    for (int j = 0; j < NFR; ++j) {
+      const int64_t n = wc0 + j * 16 + 4 * kg;
       if (n >= N) continue;
       const v4f v = acc[f][j];
       if (out_f32) {
@@ -299,13 +347,53 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(
   }
 }
 
+namespace {
+
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+// Tile width for a dense problem: one workgroup per CU, so the run takes
+// ceil(tiles / CUs) rounds of a time proportional to the tile width.  Pick the width with
+// the smaller product (ties to 256).
+#ifndef FP8Q_ALLOW_224
+#define FP8Q_ALLOW_224 0
+#endif
+int pick_nfr(int64_t M, int64_t N) {
+  // The 224-wide tile reads as much LDS per step as the 256-wide one (the kernel is
+  // bound by LDS and latency, not by the matrix cores), so it only pays once the MFMAs
+  // dominate; until then every dense problem uses 256.
+  if (!FP8Q_ALLOW_224) return 8;
+  const int64_t cus = device_cus();
+  const int64_t tm = (M + kBM - 1) / kBM;
+  const int64_t r256 = (tm * ((N + 255) / 256) + cus - 1) / cus;
+  const int64_t r224 = (tm * ((N + 223) / 224) + cus - 1) / cus;
+  return r224 * 224 < r256 * 256 ? 7 : 8;
+}
+
+}  // namespace
+
 hipError_t launch_gemm(const uint8_t *xq, const float *sa, const uint8_t *wq, const float *sb,
                        int64_t M, int64_t N, int64_t K, void *c, bool out_f32, hipStream_t stream) {
-  const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+  const int nfr = pick_nfr(M, N);
+  const int64_t bn = 32 * nfr;
+  const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + bn - 1) / bn);
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gemm_blockscaled_kernel<false>, dim3(static_cast<uint32_t>(tiles)), dim3(kThreads),
-                     0, stream, xq, sa, wq, sb, static_cast<const int32_t *>(nullptr), 1, M, N, K, c,
-                     out_f32 ? 1 : 0);
+  const dim3 grid(static_cast<uint32_t>(tiles));
+  if (nfr == 7)
+    hipLaunchKernelGGL((gemm_blockscaled_kernel<7, false>), grid, dim3(kThreads), 0, stream, xq, sa, wq, sb,
+                       static_cast<const int32_t *>(nullptr), 1, M, N, K, c, out_f32 ? 1 : 0);
+  else
+    hipLaunchKernelGGL((gemm_blockscaled_kernel<8, false>), grid, dim3(kThreads), 0, stream, xq, sa, wq, sb,
+                       static_cast<const int32_t *>(nullptr), 1, M, N, K, c, out_f32 ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -314,11 +402,16 @@ hipError_t launch_grouped_gemm(const uint8_t *xq, const float *sa, const uint8_t
                                void *c, bool out_f32, hipStream_t stream) {
   // Upper bound on sum_g ceil(n_g / 256) without reading the offsets on the host.
   const int64_t slots = (M_tot + kBM - 1) / kBM + G;
-  const int64_t tiles_n = (N + kBN - 1) / kBN;
+  const int nfr = (FP8Q_ALLOW_224 && N % 256 != 0 && N % 224 == 0) ? 7 : 8;
+  const int64_t tiles_n = (N + 32 * nfr - 1) / (32 * nfr);
   if (slots > 0x7fffffff || tiles_n > 65535 || G > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gemm_blockscaled_kernel<true>, dim3(static_cast<uint32_t>(slots), static_cast<uint32_t>(tiles_n)),
-                     dim3(kThreads), 0, stream, xq, sa, wq, sb, offsets, static_cast<int>(G), M_tot, N, K,
-                     c, out_f32 ? 1 : 0);
+  const dim3 grid(static_cast<uint32_t>(slots), static_cast<uint32_t>(tiles_n));
+  if (nfr == 7)
+    hipLaunchKernelGGL((gemm_blockscaled_kernel<7, true>), grid, dim3(kThreads), 0, stream, xq, sa, wq, sb,
+                       offsets, static_cast<int>(G), M_tot, N, K, c, out_f32 ? 1 : 0);
+  else
+    hipLaunchKernelGGL((gemm_blockscaled_kernel<8, true>), grid, dim3(kThreads), 0, stream, xq, sa, wq, sb,
+                       offsets, static_cast<int>(G), M_tot, N, K, c, out_f32 ? 1 : 0);
   return hipGetLastError();
 }
 

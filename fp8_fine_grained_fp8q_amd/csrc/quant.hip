@@ -18,14 +18,26 @@
 namespace fp8q {
 
 // ---------------------------------------------------------------------------------------
-// Activation quantizer.  One wave handles a 16-row x 128-column slab (16 tiles): four
-// 16-byte loads per lane, lane (grp = lane/16, sub = lane%16) holding chunk `sub` of rows
-// row0 + 4*i + grp, i = 0..3.  Consecutive waves take consecutive K blocks of the same
-// rows, so a 256-thread workgroup streams 16 rows x 512 contiguous BF16 columns.  The 16
-// scales of the slab are one contiguous 64-byte run of sa[kb][.].
+// Activation quantizer.  One wave handles a slab of 4*NR rows x 128*NK columns: lane
+// (grp = lane/16, sub = lane%16) holds the 16-byte chunk `sub` of rows row0 + 4*i + grp
+// (i < NR) in K blocks kb0 + k (k < NK), so each 1x128 tile is one 16-lane DPP row and
+// its amax reduces with four row_ror steps and no LDS.  All NR*NK loads are issued before
+// any conversion.  Consecutive waves take consecutive K-block groups of the same rows, so
+// a 256-thread workgroup streams 4*NR rows x 4*NK*128 contiguous BF16 columns.  The 4*NR
+// scales of a tile column are one contiguous run of sa[kb][.].
 // ---------------------------------------------------------------------------------------
+#ifndef FP8Q_ACT_NR
+#define FP8Q_ACT_NR 2
+#endif
+#ifndef FP8Q_ACT_NK
+#define FP8Q_ACT_NK 2
+#endif
+#ifndef FP8Q_ACT_NT
+#define FP8Q_ACT_NT 1
+#endif
 constexpr int kActWavesPerBlock = 4;
 
+template <int NR, int NK>
 __global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t *__restrict__ x,
                                                               int64_t M, int64_t K,
                                                               uint8_t *__restrict__ xq,
@@ -33,50 +45,62 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t *__
   const int lane = threadIdx.x & 63;
   const int64_t wave = static_cast<int64_t>(blockIdx.x) * kActWavesPerBlock + (threadIdx.x >> 6);
   const int64_t KB = K >> 7;
-  const int64_t kb = wave % KB;
-  const int64_t row0 = (wave / KB) * 16;
+  const int64_t KG = (KB + NK - 1) / NK;  // K-block groups per row slab
+  const int64_t kb0 = (wave % KG) * NK;
+  const int64_t row0 = (wave / KG) * (4 * NR);
   if (row0 >= M) return;
   const int grp = lane >> 4;
   const int sub = lane & 15;
-  const int64_t col = kb * 128 + sub * 8;
 
-  uint4 v[4];
+  uint4 v[NK][NR];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t row = row0 + 4 * i + grp;
-    if (row < M) {
-      v[i] = load16_stream(x + row * K + col);
-    } else {
-      v[i] = make_uint4(0u, 0u, 0u, 0u);
+  for (int k = 0; k < NK; ++k)
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int64_t row = row0 + 4 * i + grp;
+      const int64_t col = (kb0 + k) * 128 + sub * 8;
+      if (row < M && kb0 + k < KB) {
+        v[k][i] = FP8Q_ACT_NT ? load16_stream(x + row * K + col) : *reinterpret_cast<const uint4 *>(x + row * K + col);
+      } else {
+        v[k][i] = make_uint4(0u, 0u, 0u, 0u);
+      }
     }
-  }
-  float scale[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float amax = row16_max(absmax8(v[i]));
-    scale[i] = amax / kE4M3Max;  // IEEE division (correctly rounded)
-  }
+  for (int k = 0; k < NK; ++k) {
+    if (kb0 + k >= KB) break;
+    float scale[NR];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t row = row0 + 4 * i + grp;
-    const GroupDiv dv(scale[i]);
-    const uint2 q = quant8(v[i], dv);
-    if (row < M) *reinterpret_cast<uint2 *>(xq + row * K + col) = q;
-  }
-  // lanes sub = 0..3 of each DPP row store the scales of rows row0 + 4*sub + grp
-  if (sub < 4) {
-    const float s = sub == 0 ? scale[0] : sub == 1 ? scale[1] : sub == 2 ? scale[2] : scale[3];
-    const int64_t row = row0 + 4 * sub + grp;
-    if (row < M) sa[kb * M + row] = s;
+    for (int i = 0; i < NR; ++i) {
+      const float amax = row16_max(absmax8(v[k][i]));
+      scale[i] = amax / kE4M3Max;  // IEEE division (correctly rounded)
+    }
+    const int64_t col = (kb0 + k) * 128 + sub * 8;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int64_t row = row0 + 4 * i + grp;
+      const GroupDiv dv(scale[i]);
+      const uint2 q = quant8(v[k][i], dv);
+      if (row < M) *reinterpret_cast<uint2 *>(xq + row * K + col) = q;
+    }
+    // lanes sub < NR of each DPP row store the scales of rows row0 + 4*sub + grp
+    if (sub < NR) {
+      float s = scale[0];
+#pragma unroll
+      for (int i = 1; i < NR; ++i) s = sub == i ? scale[i] : s;
+      const int64_t row = row0 + 4 * sub + grp;
+      if (row < M) sa[(kb0 + k) * M + row] = s;
+    }
   }
 }
 
 hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, uint8_t *xq, float *sa,
                             hipStream_t stream) {
-  const int64_t waves = ((M + 15) / 16) * (K / 128);
+  constexpr int NR = FP8Q_ACT_NR, NK = FP8Q_ACT_NK;
+  const int64_t KB = K / 128;
+  const int64_t waves = ((M + 4 * NR - 1) / (4 * NR)) * ((KB + NK - 1) / NK);
   const int64_t blocks = (waves + kActWavesPerBlock - 1) / kActWavesPerBlock;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(quant_act_1x128_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+  hipLaunchKernelGGL((quant_act_1x128_kernel<NR, NK>), dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
                      stream, x, M, K, xq, sa);
   return hipGetLastError();
 }
