@@ -14,9 +14,10 @@
 // run on the vector ALU one fragment column behind the MFMAs, so the matrix core is never
 // waiting on them.
 //
-// Workgroup tile 256(M) x BN(N) with BN = 32*NFR (256 or 224, picked per shape so that the
-// tiles fill the GPU in whole rounds), K step 128 (= the scale block), 8 waves in a 4(M) x
-// 2(N) grid, each owning 64 x 16*NFR outputs (4*NFR*4 FP32 accumulator VGPRs).  The MFMA
+// Workgroup tile 256(M) x BN(N) with BN = 32*NFR, K step 128 (= the scale block), 8 waves
+// in a 4(M) x 2(N) grid, each owning 64 x 16*NFR outputs (4*NFR*4 FP32 accumulator VGPRs).
+// Dense problems use 256-wide tiles, or a column split into a 256-wide range followed by a
+// 192-wide range in the same launch when that fills the GPU's CUs in fewer rounds.  The MFMA
 // takes the weight fragment as its A operand and the activation fragment as B, so every
 // lane owns one output row m and four consecutive columns n: one activation scale per
 // fragment row and 8- or 16-byte output stores.
@@ -29,6 +30,8 @@
 // can see that reading one does not wait for the loads in flight into the other.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "fp8q_launch.h"
 
@@ -44,8 +47,8 @@ constexpr int kBK = 128;
 constexpr int kThreads = 512;
 constexpr int kGroupM = 8;  // M tiles per raster group (L2 reuse of weight panels)
 
-#ifndef FP8Q_JBARRIER
-#define FP8Q_JBARRIER 1
+#ifndef FP8Q_PRIO
+#define FP8Q_PRIO 1
 #endif
 #ifndef FP8Q_SWZ_MODE
 #define FP8Q_SWZ_MODE 1
@@ -53,7 +56,9 @@ constexpr int kGroupM = 8;  // M tiles per raster group (L2 reuse of weight pane
 // XOR swizzle of the 16-byte chunk index by row.  Mode 1 spreads rows 2i and 2i+1 over
 // the two 128-byte halves of a 256-byte bank line and pairs i over the 8 chunk slots
 // (conflict-free for 16 lanes with 64 banks of 4 bytes); mode 0 separates 8 rows.
-__device__ __forceinline__ int swz(int row) { return FP8Q_SWZ_MODE ? ((row >> 1) & 7) : (row & 7); }
+__device__ __forceinline__ int swz(int row) {
+  return FP8Q_SWZ_MODE == 2 ? 0 : FP8Q_SWZ_MODE ? ((row >> 1) & 7) : (row & 7);
+}
 
 // Buffer resource (gfx9 family layout) over `bytes` bytes at `p`; loads at or past the
 // end return zeros, which is how rows beyond the tile's valid range are filled.
@@ -76,14 +81,15 @@ __device__ __forceinline__ void stage_offsets(int64_t K, int wave, int lane, uin
   }
 }
 
-// Copy one stage (K bytes [koff, koff + 128) of 256 operand rows) into LDS.  Rows past
+// Copy one stage (K bytes [koff, koff + 128) of 64*NL operand rows) into LDS.  Rows past
 // the resource's end (a 224-row weight tile, a ragged edge) are filled with zeros by the
-// buffer bounds check without touching memory, so every wave always issues four loads and
+// buffer bounds check without touching memory, so every wave always issues NL loads and
 // the loop body stays free of branches.
+template <int NL = 4>
 __device__ __forceinline__ void stage_load(__amdgpu_buffer_rsrc_t rsrc, const uint32_t off[4], uint32_t koff,
                                            FP8Q_LDS uint8_t *lds, int wave) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NL; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FP8Q_LDS void *)(lds + (8 * i + wave) * 1024), 16,
                                              static_cast<int>(off[i]), static_cast<int>(koff), 0, 0);
 }
@@ -96,6 +102,16 @@ __device__ __forceinline__ v8i frag(const FP8Q_LDS uint8_t *lds, int row, int kg
   return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 }
 
+// s_setprio with a value known after unrolling (the builtin needs a literal).
+__device__ __forceinline__ void set_prio(int p) {
+  switch (p) {
+    case 0: __builtin_amdgcn_s_setprio(0); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    default: __builtin_amdgcn_s_setprio(3); break;
+  }
+}
+
 // Block partial of a 16x16 tile over one 128-wide K block (E4M3 x E4M3, FP32 result).
 __device__ __forceinline__ v4f mfma_block(const v8i &a, const v8i &b) {
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -106,18 +122,22 @@ struct Tile {
   int64_t m_begin;  // first row of the tile (global row index)
   int rows;         // valid rows in the tile, 1..256
   int64_t n0;       // first column
+  int64_t n_end;    // one past the last column this tile may write
+  const uint8_t *x; // activation codes, [M][K]
   const uint8_t *w; // weight matrix of the tile's expert, [N][K]
   const float *sb;  // its block scales, [N/128][K/128]
 };
 
+// Dense tile of workgroup `bid` among the tiles of width kBN covering columns
+// [n_lo, n_hi) of C.
 template <int kBN>
-__device__ __forceinline__ void dense_tile(int64_t M, int64_t N, const uint8_t *wq, const float *sb, Tile &t) {
+__device__ __forceinline__ void dense_tile(int bid, int64_t M, int64_t n_lo, int64_t n_hi, const uint8_t *wq,
+                                           const float *sb, Tile &t) {
   const int tiles_m = static_cast<int>((M + kBM - 1) / kBM);
-  const int tiles_n = static_cast<int>((N + kBN - 1) / kBN);
+  const int tiles_n = static_cast<int>((n_hi - n_lo + kBN - 1) / kBN);
   const int total = tiles_m * tiles_n;
   // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous run of
   // logical tiles (a bijection on [0, total)) so that its L2 sees neighbouring tiles.
-  const int bid = blockIdx.x;
   const int per = total / 8, rem = total % 8;
   const int xcd = bid % 8, idx = bid / 8;
   const int logical = xcd * per + (xcd < rem ? xcd : rem) + idx;
@@ -131,7 +151,8 @@ __device__ __forceinline__ void dense_tile(int64_t M, int64_t N, const uint8_t *
   const int tn = in_group / gm;
   t.m_begin = static_cast<int64_t>(tm) * kBM;
   t.rows = static_cast<int>(min(static_cast<int64_t>(kBM), M - t.m_begin));
-  t.n0 = static_cast<int64_t>(tn) * kBN;
+  t.n0 = n_lo + static_cast<int64_t>(tn) * kBN;
+  t.n_end = n_hi;
   t.w = wq;
   t.sb = sb;
 }
@@ -155,6 +176,7 @@ __device__ __forceinline__ bool grouped_tile(const int32_t *__restrict__ offsets
       t.m_begin = lo;
       t.rows = static_cast<int>(min(static_cast<int64_t>(kBM), b - lo));
       t.n0 = static_cast<int64_t>(blockIdx.y) * kBN;
+      t.n_end = N;
       t.w = wq + static_cast<int64_t>(g) * N * K;
       t.sb = sb + static_cast<int64_t>(g) * (N / 128) * (K / 128);
       return true;
@@ -164,25 +186,19 @@ __device__ __forceinline__ bool grouped_tile(const int32_t *__restrict__ offsets
   return false;
 }
 
-template <int NFR, bool kGrouped>
-__global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(
-    const uint8_t *__restrict__ xq, const float *__restrict__ sa, const uint8_t *__restrict__ wq,
-    const float *__restrict__ sb, const int32_t *__restrict__ offsets, int G, int64_t M, int64_t N,
-    int64_t K, void *__restrict__ c, int out_f32) {
+// The LDS stages of one workgroup: activation and weight tiles, double buffered.  Both
+// hold 256 rows of one 128-byte K block; narrower weight tiles leave the last rows unused.
+struct Stages {
+  FP8Q_LDS uint8_t *x0, *w0, *x1, *w1;
+};
+
+// Computes one 256 x 32*NFR tile of C.
+template <int NFR>
+__device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict__ sa, int64_t M, int64_t N,
+                                          int64_t K, void *__restrict__ c, int out_f32, const Stages &st) {
   constexpr int kBN = 32 * NFR;      // tile columns
   constexpr int kWN = 16 * NFR;      // columns per wave
-  // Both operand stages hold 256 rows; a 224-column tile leaves the last 32 W rows zero.
-  __shared__ __attribute__((aligned(1024))) uint8_t sx0[kBM * kBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t sw0[kBM * kBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t sx1[kBM * kBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t sw1[kBM * kBK];
-
-  Tile t;
-  if (kGrouped) {
-    if (!grouped_tile<kBN>(offsets, G, M, N, K, wq, sb, t)) return;
-  } else {
-    dense_tile<kBN>(M, N, wq, sb, t);
-  }
+  constexpr int kWL = kBN % 64 == 0 ? kBN / 64 : 4;  // weight-stage loads per wave
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -195,8 +211,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(
   const int kg = lane >> 4;
 
   // Operand tiles as buffer resources: rows past the valid range read as zeros.
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(xq + t.m_begin * K, static_cast<uint32_t>(t.rows * K));
-  const int rows_w = static_cast<int>(min(static_cast<int64_t>(kBN), N - t.n0));
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(t.x + t.m_begin * K, static_cast<uint32_t>(t.rows * K));
+  const int rows_w = static_cast<int>(min(static_cast<int64_t>(kBN), t.n_end - t.n0));
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(t.w + t.n0 * K, static_cast<uint32_t>(rows_w * K));
   uint32_t off[4];
   stage_offsets(K, wave, lane, off);
@@ -209,11 +225,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(
     srow[f] = static_cast<int>(t.m_begin) + (r < t.rows ? r : t.rows - 1);
   }
   // Weight-block scales: the wave's columns start in 128-column block nb0; fragment
-  // columns j >= jsplit lie in block nb0 + 1 (only possible when kWN is not 128).
+  // columns j >= jsplit lie in block nb0 + 1 (a wave spans at most two blocks).
   const int64_t wc0 = t.n0 + wn * kWN;
   const int nb0 = static_cast<int>(min(static_cast<int64_t>(NB - 1), wc0 >> 7));
   const int nb1 = min(NB - 1, nb0 + 1);
-  const int jsplit = NFR == 8 ? 8 : static_cast<int>((128 - (wc0 & 127)) >> 4);
+  const int jsplit = static_cast<int>((128 - (wc0 & 127)) >> 4);
   const float *sbrow0 = t.sb + static_cast<int64_t>(nb0) * KB;
   const float *sbrow1 = t.sb + static_cast<int64_t>(nb1) * KB;
 
@@ -226,12 +242,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(
   float sa_cur[4], sa_nxt[4];
   float sb0_cur, sb1_cur, sb0_nxt = 0.0f, sb1_nxt = 0.0f;
 
-  FP8Q_LDS uint8_t *lx0 = (FP8Q_LDS uint8_t *)sx0;
-  FP8Q_LDS uint8_t *lw0 = (FP8Q_LDS uint8_t *)sw0;
-  FP8Q_LDS uint8_t *lx1 = (FP8Q_LDS uint8_t *)sx1;
-  FP8Q_LDS uint8_t *lw1 = (FP8Q_LDS uint8_t *)sw1;
-  stage_load(rx, off, 0, lx0, wave);
-  stage_load(rw, off, 0, lw0, wave);
+  stage_load(rx, off, 0, st.x0, wave);
+  stage_load<kWL>(rw, off, 0, st.w0, wave);
 #pragma unroll
   for (int f = 0; f < 4; ++f) sa_cur[f] = sa[srow[f]];
   sb0_cur = sbrow0[0];
@@ -267,7 +279,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(
     const int kn = kb + 1 < KB ? kb + 1 : kb;
     const uint32_t koff = static_cast<uint32_t>(kn) * kBK;
     stage_load(rx, off, koff, nx, wave);
-    stage_load(rw, off, koff, nw, wave);
+    stage_load<kWL>(rw, off, koff, nw, wave);
     const float *sak = sa + static_cast<int64_t>(kn) * M;
 #pragma unroll
     for (int f = 0; f < 4; ++f) sa_nxt[f] = sak[srow[f]];
@@ -277,6 +289,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(
     for (int f = 1; f < 4; ++f) xf[f] = frag(cx, wm * 64 + f * 16 + l16, kg);
 #pragma unroll
     for (int j = 0; j < NFR; ++j) {
+#if FP8Q_PRIO
+      // Progress-based issue priority: the two waves sharing a SIMD compete for its matrix
+      // core, and by default the older one wins every time and runs ahead, leaving the
+      // younger one alone (and the matrix core under-fed) before each barrier.  Lowering
+      // the priority as a wave moves through the block lets the one behind catch up.
+      if (j == 0 || (j * 4) / NFR != ((j - 1) * 4) / NFR) set_prio(3 - (j * 4) / NFR);
+#endif
       const v8i wf = wnext;
       if (j + 1 < NFR) wnext = frag(cw, wn * kWN + (j + 1) * 16 + l16, kg);
       v4f np[4];
@@ -291,9 +310,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(
         for (int i = 0; i < 4; ++i) acc[f][jp][i] = __builtin_fmaf(pp[f][i], sc, acc[f][jp][i]);
         pp[f] = np[f];
       }
-#if FP8Q_JBARRIER
+      // Issue order within a column: each MFMA follows a group of promotion FMAs of the
+      // previous column, so the vector ALU work sits between the matrix instructions.
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // 5 VALU
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      }
       __builtin_amdgcn_sched_barrier(0);
-#endif
     }
     const float sbl = NFR - 1 < jsplit ? sb0_cur : sb1_cur;
 #pragma unroll
@@ -307,10 +331,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(
 
   int kb = 0;
   for (; kb + 1 < KB; kb += 2) {
-    step(lx0, lw0, lx1, lw1, kb);
-    step(lx1, lw1, lx0, lw0, kb + 1);
+    step(st.x0, st.w0, st.x1, st.w1, kb);
+    step(st.x1, st.w1, st.x0, st.w0, kb + 1);
   }
-  if (kb < KB) step(lx0, lw0, lx1, lw1, kb);
+  if (kb < KB) step(st.x0, st.w0, st.x1, st.w1, kb);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the last (repeated) copy
 #pragma unroll
   for (int f = 0; f < 4; ++f)
@@ -327,7 +351,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(
 #pragma unroll
     for (int j = 0; j < NFR; ++j) {
       const int64_t n = wc0 + j * 16 + 4 * kg;
-      if (n >= N) continue;
+      if (n >= t.n_end) continue;
       const v4f v = acc[f][j];
       if (out_f32) {
         *reinterpret_cast<v4f *>(static_cast<float *>(c) + m * N + n) = v;
@@ -347,6 +371,55 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(
   }
 }
 
+#define FP8Q_DECLARE_STAGES(st)                                          \
+  __shared__ __attribute__((aligned(1024))) uint8_t sx0[kBM * kBK];      \
+  __shared__ __attribute__((aligned(1024))) uint8_t sw0[kBM * kBK];      \
+  __shared__ __attribute__((aligned(1024))) uint8_t sx1[kBM * kBK];      \
+  __shared__ __attribute__((aligned(1024))) uint8_t sw1[kBM * kBK];      \
+  const Stages st = {(FP8Q_LDS uint8_t *)sx0, (FP8Q_LDS uint8_t *)sw0,   \
+                     (FP8Q_LDS uint8_t *)sx1, (FP8Q_LDS uint8_t *)sw1}
+
+// One tile width for the whole problem (dense: 1-D grid; grouped: see grouped_tile).
+template <int NFR, bool kGrouped>
+__global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(
+    const uint8_t *__restrict__ xq, const float *__restrict__ sa, const uint8_t *__restrict__ wq,
+    const float *__restrict__ sb, const int32_t *__restrict__ offsets, int G, int64_t M, int64_t N,
+    int64_t K, void *__restrict__ c, int out_f32) {
+  FP8Q_DECLARE_STAGES(st);
+  Tile t;
+  if (kGrouped) {
+    if (!grouped_tile<32 * NFR>(offsets, G, M, N, K, wq, sb, t)) return;
+  } else {
+    dense_tile<32 * NFR>(blockIdx.x, M, 0, N, wq, sb, t);
+  }
+  t.x = xq;
+  gemm_tile<NFR>(t, sa, M, N, K, c, out_f32, st);
+}
+
+// Dense problem in two column ranges of different tile widths, one launch: workgroups
+// [0, tiles1) cover columns [0, n_split) with 32*NFR1-wide tiles, the rest cover
+// [n_split, N) with 32*NFR2-wide tiles.  Workgroups start in index order, so the wide
+// tiles take the first round and the narrow ones fill what would otherwise be a partly
+// idle last round.
+template <int NFR1, int NFR2>
+__global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_split_kernel(
+    const uint8_t *__restrict__ xq, const float *__restrict__ sa, const uint8_t *__restrict__ wq,
+    const float *__restrict__ sb, int64_t M, int64_t N, int64_t K, int64_t n_split, int tiles1,
+    void *__restrict__ c, int out_f32) {
+  FP8Q_DECLARE_STAGES(st);
+  Tile t;
+  const int bid = blockIdx.x;
+  if (bid < tiles1) {
+    dense_tile<32 * NFR1>(bid, M, 0, n_split, wq, sb, t);
+    t.x = xq;
+    gemm_tile<NFR1>(t, sa, M, N, K, c, out_f32, st);
+  } else {
+    dense_tile<32 * NFR2>(bid - tiles1, M, n_split, N, wq, sb, t);
+    t.x = xq;
+    gemm_tile<NFR2>(t, sa, M, N, K, c, out_f32, st);
+  }
+}
+
 namespace {
 
 int device_cus() {
@@ -361,39 +434,74 @@ int device_cus() {
   return cus[dev];
 }
 
-// Tile width for a dense problem: one workgroup per CU, so the run takes
-// ceil(tiles / CUs) rounds of a time proportional to the tile width.  Pick the width with
-// the smaller product (ties to 256).
-#ifndef FP8Q_ALLOW_224
-#define FP8Q_ALLOW_224 0
+#ifndef FP8Q_NARROW_COST
+#define FP8Q_NARROW_COST 0.82
 #endif
-int pick_nfr(int64_t M, int64_t N) {
-  // The 224-wide tile reads as much LDS per step as the 256-wide one (the kernel is
-  // bound by LDS and latency, not by the matrix cores), so it only pays once the MFMAs
-  // dominate; until then every dense problem uses 256.
-  if (!FP8Q_ALLOW_224) return 8;
-  const int64_t cus = device_cus();
-  const int64_t tm = (M + kBM - 1) / kBM;
-  const int64_t r256 = (tm * ((N + 255) / 256) + cus - 1) / cus;
-  const int64_t r224 = (tm * ((N + 223) / 224) + cus - 1) / cus;
-  return r224 * 224 < r256 * 256 ? 7 : 8;
+
+// Finish time of `n1` tiles of cost 1 followed by `n2` tiles of cost c2 when each tile
+// goes, in order, to the first of `cus` CUs that becomes free.  After the first kind the
+// CUs' free times take two values, so the simulation walks two classes of CUs.
+double makespan(int64_t n1, int64_t n2, double c2, int64_t cus) {
+  const int64_t f = n1 / cus, r = n1 % cus;
+  double end = static_cast<double>(f + (r ? 1 : 0));
+  double t[2] = {static_cast<double>(f), static_cast<double>(f + 1)};
+  const int64_t cnt[2] = {cus - r, r};
+  for (int64_t left = n2; left > 0;) {
+    const int i = (cnt[1] == 0 || (cnt[0] > 0 && t[0] <= t[1])) ? 0 : 1;
+    left -= min(left, cnt[i]);
+    end = t[i] + c2 > end ? t[i] + c2 : end;
+    t[i] += c2;
+  }
+  return end;
 }
 
 }  // namespace
 
+#ifndef FP8Q_SPLIT
+#define FP8Q_SPLIT 1
+#endif
+
 hipError_t launch_gemm(const uint8_t *xq, const float *sa, const uint8_t *wq, const float *sb,
                        int64_t M, int64_t N, int64_t K, void *c, bool out_f32, hipStream_t stream) {
-  const int nfr = pick_nfr(M, N);
-  const int64_t bn = 32 * nfr;
-  const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + bn - 1) / bn);
+  const int64_t cus = device_cus();
+  const int64_t tm = (M + kBM - 1) / kBM;
+  const int64_t tiles = tm * ((N + 255) / 256);
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<uint32_t>(tiles));
-  if (nfr == 7)
-    hipLaunchKernelGGL((gemm_blockscaled_kernel<7, false>), grid, dim3(kThreads), 0, stream, xq, sa, wq, sb,
-                       static_cast<const int32_t *>(nullptr), 1, M, N, K, c, out_f32 ? 1 : 0);
-  else
-    hipLaunchKernelGGL((gemm_blockscaled_kernel<8, false>), grid, dim3(kThreads), 0, stream, xq, sa, wq, sb,
-                       static_cast<const int32_t *>(nullptr), 1, M, N, K, c, out_f32 ? 1 : 0);
+  // Uniform 256-wide tiles, or the first a*256 columns in 256-wide tiles and the rest in
+  // 192-wide ones, whichever finishes first by the cost model (a 192-wide tile costs
+  // FP8Q_NARROW_COST of a 256-wide one: fewer MFMAs, nearly the same copies per step).
+  double best = makespan(tiles, 0, 0.0, cus);
+  int64_t best_a = -1;
+  // FP8Q_DENSE_SPLIT overrides the choice (for tests): "off" = uniform 256-wide tiles, an
+  // integer a >= 0 = split after a*256 columns (clamped below N).
+  const char *force = getenv("FP8Q_DENSE_SPLIT");
+  if (force && force[0] && strcmp(force, "auto") != 0) {
+    if (strcmp(force, "off") != 0) {
+      const long long a = atoll(force);
+      best_a = a < 0 ? 0 : (a * 256 < N ? a : (N - 1) / 256);
+    }
+  } else if (FP8Q_SPLIT && tiles <= 8 * cus) {
+    // Past a few rounds the idle part of the last round is a small share of the run.
+    for (int64_t a = 0; a * 256 < N; ++a) {
+      const int64_t n2 = tm * ((N - a * 256 + 191) / 192);
+      const double ms = makespan(tm * a, n2, FP8Q_NARROW_COST, cus);
+      if (ms < best * 0.97) {
+        best = ms;
+        best_a = a;
+      }
+    }
+  }
+  if (best_a < 0) {
+    hipLaunchKernelGGL((gemm_blockscaled_kernel<8, false>), dim3(static_cast<uint32_t>(tiles)), dim3(kThreads), 0,
+                       stream, xq, sa, wq, sb, static_cast<const int32_t *>(nullptr), 1, M, N, K, c,
+                       out_f32 ? 1 : 0);
+  } else {
+    const int64_t t1 = tm * best_a;
+    const int64_t t2 = tm * ((N - best_a * 256 + 191) / 192);
+    if (t1 + t2 > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_blockscaled_split_kernel<8, 6>), dim3(static_cast<uint32_t>(t1 + t2)), dim3(kThreads),
+                       0, stream, xq, sa, wq, sb, M, N, K, best_a * 256, static_cast<int>(t1), c, out_f32 ? 1 : 0);
+  }
   return hipGetLastError();
 }
 
@@ -402,16 +510,11 @@ hipError_t launch_grouped_gemm(const uint8_t *xq, const float *sa, const uint8_t
                                void *c, bool out_f32, hipStream_t stream) {
   // Upper bound on sum_g ceil(n_g / 256) without reading the offsets on the host.
   const int64_t slots = (M_tot + kBM - 1) / kBM + G;
-  const int nfr = (FP8Q_ALLOW_224 && N % 256 != 0 && N % 224 == 0) ? 7 : 8;
-  const int64_t tiles_n = (N + 32 * nfr - 1) / (32 * nfr);
+  const int64_t tiles_n = (N + 255) / 256;
   if (slots > 0x7fffffff || tiles_n > 65535 || G > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid(static_cast<uint32_t>(slots), static_cast<uint32_t>(tiles_n));
-  if (nfr == 7)
-    hipLaunchKernelGGL((gemm_blockscaled_kernel<7, true>), grid, dim3(kThreads), 0, stream, xq, sa, wq, sb,
-                       offsets, static_cast<int>(G), M_tot, N, K, c, out_f32 ? 1 : 0);
-  else
-    hipLaunchKernelGGL((gemm_blockscaled_kernel<8, true>), grid, dim3(kThreads), 0, stream, xq, sa, wq, sb,
-                       offsets, static_cast<int>(G), M_tot, N, K, c, out_f32 ? 1 : 0);
+  hipLaunchKernelGGL((gemm_blockscaled_kernel<8, true>), grid, dim3(kThreads), 0, stream, xq, sa, wq, sb, offsets,
+                     static_cast<int>(G), M_tot, N, K, c, out_f32 ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -8,7 +8,8 @@ integer case (bit-exact, pins the MFMA operand and output layouts), a characteri
 the matrix core's own block summation, the dense 4096x7168x7168
 workload in the benchmarked launch (every output), grouped MoE shapes with
 empty / 1 / 127..257-row experts, the MoE up/down workloads (sampled experts), run-to-run
-determinism and untouched rows outside every expert range."""
+determinism, the dense tile plans (uniform 256-wide tiles or a 256/192-wide column split,
+bit-identical to each other) and untouched rows outside every expert range."""
 import numpy as np
 import pytest
 import torch
@@ -106,6 +107,28 @@ def test_block_partial_precision_with_a_dominant_product():
     assert_gemm_within_tol(got, ref, og.row_norms_act(xq, sa), og.row_norms_w(wq, sb), "dominant product")
 
 
+PLANS = ["off", "0", "1", "2", "auto"]
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 1152, 1024), (257, 640, 384), (40, 128, 256)])
+def test_dense_tile_plans(M, N, K, monkeypatch):
+    """Dense launches either use 256-wide tiles throughout ("off") or split the columns
+    into a 256-wide range [0, a*256) and a 192-wide range after it (a = 0, 1, 2), one
+    workgroup index range each; "auto" is the library's own choice.  Every plan must meet
+    the bar, and since a tile's width does not change the arithmetic of any output (same
+    block partials, same FMA order), all plans must give bit-identical results."""
+    xq, sa, wq, sb = quantized(M, N, K, seed=7 * M + N + K, xscale=2.0)
+    ref = og.gemm_blockscaled(xq, sa, wq, sb)
+    xn, wn = og.row_norms_act(xq, sa), og.row_norms_w(wq, sb)
+    outs = {}
+    for plan in PLANS:
+        monkeypatch.setenv("FP8Q_DENSE_SPLIT", plan)
+        outs[plan] = gpu_gemm(xq, sa, wq, sb, torch.float32)
+        assert_gemm_within_tol(outs[plan], ref, xn, wn, f"{M}x{N}x{K} plan {plan}")
+    for plan in PLANS[1:]:
+        assert np.array_equal(outs[plan], outs["off"]), plan
+
+
 def test_deterministic():
     xq, sa, wq, sb = quantized(300, 640, 512, seed=5)
     a = fq.fp8q_gemm_blockscaled(dev(xq), dev(sa), dev(wq), dev(sb))
@@ -142,6 +165,17 @@ def test_dense_full_size_repeatable(dense_quantized):
         again = fq.fp8q_gemm_blockscaled(xq, sa, wq, sb)
         torch.cuda.synchronize()
         assert torch.equal(first.view(torch.int16), again.view(torch.int16))
+
+
+def test_dense_full_size_plans_agree(dense_quantized, monkeypatch):
+    """At full size the benchmarked (automatic) plan and the uniform 256-wide plan give
+    bit-identical output."""
+    xq, sa, wq, sb = (dev(a) for a in dense_quantized)
+    auto = fq.fp8q_gemm_blockscaled(xq, sa, wq, sb)
+    monkeypatch.setenv("FP8Q_DENSE_SPLIT", "off")
+    uniform = fq.fp8q_gemm_blockscaled(xq, sa, wq, sb)
+    torch.cuda.synchronize()
+    assert torch.equal(auto.view(torch.int16), uniform.view(torch.int16))
 
 
 def run_grouped(xq, sa, wq, sb, offsets, out_dtype=torch.bfloat16, fill=None):
