@@ -79,9 +79,9 @@ def measured_traffic(workload: str):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("gemm_source_sha256_16") != source_hash() or t.get("workload") != workload:
+    if t.get("gemm_source_sha256_16") != source_hash():
         return None
-    return t.get("bytes_per_launch")
+    return t.get("workloads", {}).get(workload, {}).get("bytes_per_launch")
 
 
 def cpu_baseline(cfg, flops_step):
