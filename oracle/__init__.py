@@ -34,5 +34,7 @@ Modules:
     e4m3   -- OCP E4M3 (E4M3FN) decode / encode (nearest, ties to even, saturating)
     quant  -- 1x128 activation-tile and 128x128 weight-block online quantizers
     gemm   -- dequantized FP64 GEMM, dense and grouped, and the acceptance bound
+    backward -- dgrad / wgrad of a linear layer: transposed weight blocks, 128x1
+              token tiles, the GEMM with per-row scales on both operands
 """
-from . import e4m3, quant, gemm  # noqa: F401
+from . import e4m3, quant, gemm, backward  # noqa: F401
