@@ -9,7 +9,11 @@ One step = one pass of the whole path over one batch of synthetic input:
        grouped over experts for the MoE workloads.
 Default workload: the dense projection X[4096x7168] x W[7168x7168]^T, BF16 out.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense|large|moe_up|moe_down]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense|large|moe_up|moe_down|train]
+
+The `train` workload runs one training step of the dense layer instead: both-orientation
+quantization of X and dY, the transposing weight quantizer, and the three GEMMs (forward,
+dgrad through the W^T blocks, wgrad over token tiles); value = 3*2*M*N*K FLOPs per step.
 
 Prints ONE JSON line.  `value` = 2*M*N*K*steps / (timed wall time of the steps), i.e. GEMM
 TFLOP/s including both online quantizers.  Inputs are resident in HBM before timing.  To
@@ -45,6 +49,8 @@ WORKLOADS = {
     "large": "large fused pipeline X[16384x7168] (Student-t 3) . W[18432x7168]^T, fp32 out",
     "moe_up": "MoE up-projection, 32 local experts of 256 (top-8 routing of 8192 tokens), W[32][4096x7168], bf16 out",
     "moe_down": "MoE down-projection, 32 local experts, SiLU(g)*u inputs [n x 2048], W[32][7168x2048], bf16 out",
+    "train": "training step of the dense projection X[4096x7168], W[7168x7168]: forward Y = X W^T (bf16), "
+             "dgrad dX = dY W (bf16), wgrad dW = dY^T X over the 4096 tokens (fp32)",
 }
 
 
@@ -129,6 +135,82 @@ def cpu_baseline(cfg, flops_step):
             "sample": sample, "seconds_measured": round(t3 - t0, 2), "seconds_per_step_extrapolated": round(t_step, 2)}
 
 
+def run_train(args, torch, fq, dev):
+    """The `train` workload (see the module docstring)."""
+    cfg = gen("train")
+    M, K = cfg["x"].shape
+    N = cfg["w"].shape[1]
+    flops = 3 * 2.0 * M * N * K
+    x0 = torch.from_numpy(cfg["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+    w0 = torch.from_numpy(cfg["w"][0].view(np.int16)).view(torch.bfloat16).to(dev)
+    dy0 = torch.from_numpy(cfg["dy"].view(np.int16)).view(torch.bfloat16).to(dev)
+    per_set = 2 * (x0.numel() + w0.numel() + dy0.numel()) * 2 + 4 * N * K
+    nsets = min(8, args.sets or max(2, int(np.ceil(3 * 256e6 / per_set))))
+    u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
+    sets = []
+    for i in range(nsets):
+        sets.append({
+            "x": x0 if i == 0 else x0.clone(), "w": w0 if i == 0 else w0.clone(), "dy": dy0 if i == 0 else dy0.clone(),
+            "xq": torch.empty((M, K), dtype=u8, device=dev), "sa": torch.empty((K // 128, M), dtype=f32, device=dev),
+            "xqt": torch.empty((K, M), dtype=u8, device=dev), "sat": torch.empty((M // 128, K), dtype=f32, device=dev),
+            "wq": torch.empty((N, K), dtype=u8, device=dev), "sb": torch.empty((N // 128, K // 128), dtype=f32, device=dev),
+            "wqt": torch.empty((K, N), dtype=u8, device=dev), "sbt": torch.empty((K // 128, N // 128), dtype=f32, device=dev),
+            "dyq": torch.empty((M, N), dtype=u8, device=dev), "sdy": torch.empty((N // 128, M), dtype=f32, device=dev),
+            "dyqt": torch.empty((N, M), dtype=u8, device=dev), "sdyt": torch.empty((M // 128, N), dtype=f32, device=dev),
+            "y": torch.empty((M, N), dtype=bf, device=dev), "dx": torch.empty((M, K), dtype=bf, device=dev),
+            "dw": torch.empty((N, K), dtype=f32, device=dev),
+        })
+    stream = torch.cuda.current_stream()
+    names = ["quant_act_dual(X)", "quant_w_t(W)", "gemm fwd", "quant_act_dual(dY)", "gemm dgrad", "gemm_rowscaled wgrad"]
+
+    def step(s, ev=None):
+        calls = [
+            lambda: fq.fp8q_quantize_act_dual(s["x"], s["xq"], s["sa"], s["xqt"], s["sat"], stream=stream),
+            lambda: fq.fp8q_quantize_w_128x128_t(s["w"], s["wq"], s["sb"], s["wqt"], s["sbt"], stream=stream),
+            lambda: fq.fp8q_gemm_blockscaled(s["xq"], s["sa"], s["wq"], s["sb"], out=s["y"], stream=stream),
+            lambda: fq.fp8q_quantize_act_dual(s["dy"], s["dyq"], s["sdy"], s["dyqt"], s["sdyt"], stream=stream),
+            lambda: fq.fp8q_gemm_blockscaled(s["dyq"], s["sdy"], s["wqt"], s["sbt"], out=s["dx"], stream=stream),
+            lambda: fq.fp8q_gemm_rowscaled(s["dyqt"], s["sdyt"], s["xqt"], s["sat"], out=s["dw"], stream=stream),
+        ]
+        for i, c in enumerate(calls):
+            if ev is not None:
+                ev[i].record(stream)
+            c()
+        if ev is not None:
+            ev[len(calls)].record(stream)
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % nsets], evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)])) * 1e3
+           for j, n in enumerate(names)}
+    gemm_flops = 2.0 * M * N * K
+    tflops = {n: round(gemm_flops / (per[n] * 1e-6) / 1e12, 1) for n in names if n.startswith("gemm")}
+    dom = max((n for n in names if n.startswith("gemm")), key=lambda n: per[n])
+    value = flops * args.steps / wall / 1e12
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic (seeded; shapes and distributions of the workload, no dataset)",
+        "config": {"workload": WORKLOADS["train"], "M": M, "N": N, "K": K, "buffer_sets": nsets},
+        "pct_fp8_peak_step": round(value / PEAK_FP8_TFLOPS * 100, 2),
+        "kernels_us": {n: round(v, 2) for n, v in per.items()},
+        "gemm_tflops": tflops,
+        "roofline": {"bound": "mfma", "achieved": tflops[dom], "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops[dom] / PEAK_FP8_TFLOPS, 4), "traffic": None, "kernel": dom,
+                     "flop_per_launch": gemm_flops, "avg_launch_us": round(per[dom], 2)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -144,6 +226,9 @@ def main():
         sys.exit(1)
     fq.load_library()
     dev = torch.device("cuda:0")
+    if args.workload == "train":
+        run_train(args, torch, fq, dev)
+        return
 
     t_gen = time.perf_counter()
     cfg = gen(args.workload)

@@ -11,6 +11,12 @@ missing or no GPU is present the calls raise.
     c = fp8q_gemm_blockscaled(xq, sa, wq, sb)      # bf16 [M, N] (or out_dtype=torch.float32)
     c = fp8q_grouped_gemm_blockscaled(xq, sa, wq, sb, offsets)   # offsets: int32 [G+1] on cuda
 
+Backward pass (same E4M3 format):
+    wq, sb, wqt, sbt = fp8q_quantize_w_128x128_t(w)   # also W^T codes / scales
+    dx = fp8q_gemm_blockscaled(dyq, sa_dy, wqt, sbt)    # dgrad dX = dY W
+    xq, sa, xqt, sat = fp8q_quantize_act_dual(x)        # tiles along K and along the tokens
+    dw = fp8q_gemm_rowscaled(dyqt, sat_dy, xqt, sat)    # wgrad dW = dY^T X
+
 Layouts: xq uint8 [M, K]; sa float32 [K/128, M]; wq uint8 [G, N, K]; sb float32
 [G, N/128, K/128]; C row-major [M, N].
 """
@@ -28,10 +34,11 @@ LIB_PATH = os.environ.get("FP8Q_LIBRARY") or os.path.join(HERE, "libfp8q.so")
 FP8Q_OK = 0
 FP8Q_OUT_BF16 = 0
 FP8Q_OUT_F32 = 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 EXPORTED = ("fp8q_quantize_act_1x128", "fp8q_quantize_w_128x128", "fp8q_gemm_blockscaled",
-            "fp8q_grouped_gemm_blockscaled", "fp8q_status_string", "fp8q_abi_version")
+            "fp8q_grouped_gemm_blockscaled", "fp8q_quantize_w_128x128_t", "fp8q_quantize_act_dual",
+            "fp8q_gemm_rowscaled", "fp8q_status_string", "fp8q_abi_version")
 
 
 class Fp8qError(RuntimeError):
@@ -57,8 +64,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp8q_quantize_w_128x128.argtypes = [vp, i64, i64, i64, vp, vp, vp]
     lib.fp8q_gemm_blockscaled.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i32, vp]
     lib.fp8q_grouped_gemm_blockscaled.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp]
+    lib.fp8q_quantize_w_128x128_t.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp]
+    lib.fp8q_quantize_act_dual.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
+    lib.fp8q_gemm_rowscaled.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i32, vp]
     for name in ("fp8q_quantize_act_1x128", "fp8q_quantize_w_128x128", "fp8q_gemm_blockscaled",
-                 "fp8q_grouped_gemm_blockscaled"):
+                 "fp8q_grouped_gemm_blockscaled", "fp8q_quantize_w_128x128_t", "fp8q_quantize_act_dual",
+                 "fp8q_gemm_rowscaled"):
         getattr(lib, name).restype = i32
     lib.fp8q_status_string.argtypes = [i32]
     lib.fp8q_status_string.restype = ctypes.c_char_p
@@ -169,7 +180,58 @@ def fp8q_grouped_gemm_blockscaled(xq, sa, wq, sb, offsets, out_dtype=torch.bfloa
     return out
 
 
+def fp8q_quantize_w_128x128_t(w: torch.Tensor, wq=None, sb=None, wqt=None, sbt=None, stream=None):
+    """128x128 blocks of w [G, N, K] (or [N, K]) -> (wq, sb, wqt, sbt): the codes and scales
+    of w and of its transpose (wqt uint8 [G, K, N], sbt float32 [G, K/128, N/128])."""
+    _need(w, torch.bfloat16, "w")
+    squeeze = w.dim() == 2
+    G, N, K = (1, *w.shape) if squeeze else w.shape
+    lead = () if squeeze else (G,)
+    dev = w.device
+    wq = torch.empty(w.shape, dtype=torch.uint8, device=dev) if wq is None else wq
+    sb = torch.empty(lead + (N // 128, K // 128), dtype=torch.float32, device=dev) if sb is None else sb
+    wqt = torch.empty(lead + (K, N), dtype=torch.uint8, device=dev) if wqt is None else wqt
+    sbt = torch.empty(lead + (K // 128, N // 128), dtype=torch.float32, device=dev) if sbt is None else sbt
+    _check(load_library().fp8q_quantize_w_128x128_t(_ptr(w), G, N, K, _ptr(wq), _ptr(sb), _ptr(wqt), _ptr(sbt),
+                                                    _stream(stream)), "fp8q_quantize_w_128x128_t")
+    return wq, sb, wqt, sbt
+
+
+def fp8q_quantize_act_dual(x: torch.Tensor, xq=None, sa=None, xqt=None, sat=None, stream=None):
+    """x bf16 [M, K] (M % 128 == 0) -> (xq [M, K], sa [K/128, M], xqt [K, M], sat [M/128, K]):
+    1x128 tiles along K and tiles of 128 tokens along M (codes channel-major)."""
+    _need(x, torch.bfloat16, "x")
+    M, K = x.shape
+    dev = x.device
+    xq = torch.empty((M, K), dtype=torch.uint8, device=dev) if xq is None else xq
+    sa = torch.empty((K // 128, M), dtype=torch.float32, device=dev) if sa is None else sa
+    xqt = torch.empty((K, M), dtype=torch.uint8, device=dev) if xqt is None else xqt
+    sat = torch.empty((M // 128, K), dtype=torch.float32, device=dev) if sat is None else sat
+    _check(load_library().fp8q_quantize_act_dual(_ptr(x), M, K, _ptr(xq), _ptr(sa), _ptr(xqt), _ptr(sat),
+                                                 _stream(stream)), "fp8q_quantize_act_dual")
+    return xq, sa, xqt, sat
+
+
+def fp8q_gemm_rowscaled(aq, sa, bq, sb, out_dtype=torch.bfloat16, out: torch.Tensor | None = None, stream=None):
+    """C [P, Q] = dequant(aq, sa) @ dequant(bq, sb)^T with 1x128 row scales on both operands:
+    aq [P, Kc], sa [Kc/128, P], bq [Q, Kc], sb [Kc/128, Q]."""
+    _need(aq, torch.uint8, "aq")
+    _need(bq, torch.uint8, "bq")
+    _need(sa, torch.float32, "sa")
+    _need(sb, torch.float32, "sb")
+    P, Kc = aq.shape
+    Q = bq.shape[0]
+    if out is None:
+        out = torch.empty((P, Q), dtype=out_dtype, device=aq.device)
+    _check(load_library().fp8q_gemm_rowscaled(_ptr(aq), _ptr(sa), _ptr(bq), _ptr(sb), P, Q, Kc, _ptr(out),
+                                              _out_code(out.dtype), _stream(stream)), "fp8q_gemm_rowscaled")
+    return out
+
+
 quantize_act_1x128 = fp8q_quantize_act_1x128
 quantize_w_128x128 = fp8q_quantize_w_128x128
 gemm_blockscaled = fp8q_gemm_blockscaled
 grouped_gemm_blockscaled = fp8q_grouped_gemm_blockscaled
+quantize_w_128x128_t = fp8q_quantize_w_128x128_t
+quantize_act_dual = fp8q_quantize_act_dual
+gemm_rowscaled = fp8q_gemm_rowscaled

@@ -63,7 +63,7 @@ fp8q_status fp8q_quantize_w_128x128(const uint16_t *w_bf16, int64_t G, int64_t N
   if (!w_bf16 || !wq || !sb) return FP8Q_ERR_NULL;
   if (misaligned(w_bf16) || misaligned(wq) || misaligned(sb)) return FP8Q_ERR_ALIGN;
   if (device_ok() != FP8Q_OK) return FP8Q_ERR_DEVICE;
-  return launched(fp8q::launch_quant_w(w_bf16, G, N, K, wq, sb, as_stream(stream)));
+  return launched(fp8q::launch_quant_w(w_bf16, G, N, K, wq, sb, nullptr, nullptr, as_stream(stream)));
 }
 
 fp8q_status fp8q_gemm_blockscaled(const uint8_t *xq, const float *sa, const uint8_t *wq,
@@ -92,11 +92,47 @@ fp8q_status fp8q_grouped_gemm_blockscaled(const uint8_t *xq, const float *sa, co
                                             out_dtype == FP8Q_OUT_F32, as_stream(stream)));
 }
 
+fp8q_status fp8q_quantize_w_128x128_t(const uint16_t *w_bf16, int64_t G, int64_t N, int64_t K,
+                                      uint8_t *wq, float *sb, uint8_t *wqt, float *sbt, void *stream) {
+  if (G < 1 || bad_dim(G) || bad_dim(N) || bad_dim(K)) return FP8Q_ERR_SHAPE;
+  if (N % 128 != 0 || K % 128 != 0) return FP8Q_ERR_SHAPE;
+  if (too_many(G, N) || too_many(G * N, K)) return FP8Q_ERR_SHAPE;
+  if (N == 0 || K == 0) return FP8Q_OK;
+  if (!w_bf16 || !wq || !sb || !wqt || !sbt) return FP8Q_ERR_NULL;
+  if (misaligned(w_bf16) || misaligned(wq) || misaligned(sb) || misaligned(wqt) || misaligned(sbt))
+    return FP8Q_ERR_ALIGN;
+  if (device_ok() != FP8Q_OK) return FP8Q_ERR_DEVICE;
+  return launched(fp8q::launch_quant_w(w_bf16, G, N, K, wq, sb, wqt, sbt, as_stream(stream)));
+}
+
+fp8q_status fp8q_quantize_act_dual(const uint16_t *x_bf16, int64_t M, int64_t K, uint8_t *xq,
+                                   float *sa, uint8_t *xqt, float *sat, void *stream) {
+  if (bad_dim(M) || bad_dim(K) || M % 128 != 0 || K % 128 != 0 || too_many(M, K)) return FP8Q_ERR_SHAPE;
+  if (M == 0 || K == 0) return FP8Q_OK;
+  if (!x_bf16 || !xq || !sa || !xqt || !sat) return FP8Q_ERR_NULL;
+  if (misaligned(x_bf16) || misaligned(xq) || misaligned(sa) || misaligned(xqt) || misaligned(sat))
+    return FP8Q_ERR_ALIGN;
+  if (device_ok() != FP8Q_OK) return FP8Q_ERR_DEVICE;
+  return launched(fp8q::launch_quant_act_dual(x_bf16, M, K, xq, sa, xqt, sat, as_stream(stream)));
+}
+
+fp8q_status fp8q_gemm_rowscaled(const uint8_t *aq, const float *sa, const uint8_t *bq, const float *sb,
+                                int64_t P, int64_t Q, int64_t Kc, void *c, int32_t out_dtype,
+                                void *stream) {
+  const fp8q_status st = check_gemm(aq, sa, bq, sb, P, Q, Kc, c, out_dtype);
+  if (st < 0) return st;
+  if ((Kc / 128) * Q >= (int64_t(1) << 29)) return FP8Q_ERR_SHAPE;  // scale offsets fit 31 bits
+  if (st > 0) return FP8Q_OK;
+  if (device_ok() != FP8Q_OK) return FP8Q_ERR_DEVICE;
+  return launched(fp8q::launch_gemm_rowscaled(aq, sa, bq, sb, P, Q, Kc, c, out_dtype == FP8Q_OUT_F32,
+                                              as_stream(stream)));
+}
+
 const char *fp8q_status_string(fp8q_status status) {
   switch (status) {
     case FP8Q_OK: return "ok";
     case FP8Q_ERR_NULL: return "null pointer argument";
-    case FP8Q_ERR_SHAPE: return "invalid shape (negative, K/N not a multiple of 128, G < 1, or too large)";
+    case FP8Q_ERR_SHAPE: return "invalid shape (negative, K/N (or M for the dual quantizer) not a multiple of 128, G < 1, or too large)";
     case FP8Q_ERR_ALIGN: return "misaligned pointer (16-byte alignment required; offsets 4-byte)";
     case FP8Q_ERR_DTYPE: return "invalid out_dtype";
     case FP8Q_ERR_DEVICE: return "no usable HIP device";

@@ -10,11 +10,21 @@ namespace fp8q {
 hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, uint8_t *xq, float *sa,
                             hipStream_t stream);
 
+// wqt / sbt (W^T codes and block scales) are written too unless wqt is null.
 hipError_t launch_quant_w(const uint16_t *w, int64_t G, int64_t N, int64_t K, uint8_t *wq, float *sb,
-                          hipStream_t stream);
+                          uint8_t *wqt, float *sbt, hipStream_t stream);
+
+// Both orientations of X[M][K] (M % 128 == 0): 1x128 tiles along K (xq, sa as above)
+// and 128x1 tiles along M, codes channel-major xqt[K][M], scales sat[M/128][K].
+hipError_t launch_quant_act_dual(const uint16_t *x, int64_t M, int64_t K, uint8_t *xq, float *sa,
+                                 uint8_t *xqt, float *sat, hipStream_t stream);
 
 hipError_t launch_gemm(const uint8_t *xq, const float *sa, const uint8_t *wq, const float *sb,
                        int64_t M, int64_t N, int64_t K, void *c, bool out_f32, hipStream_t stream);
+
+// C = dequant(aq, sa) dequant(bq, sb)^T, both with 1x128 row scales ([K/128][rows]).
+hipError_t launch_gemm_rowscaled(const uint8_t *aq, const float *sa, const uint8_t *bq, const float *sb,
+                                 int64_t M, int64_t N, int64_t K, void *c, bool out_f32, hipStream_t stream);
 
 hipError_t launch_grouped_gemm(const uint8_t *xq, const float *sa, const uint8_t *wq, const float *sb,
                                const int32_t *offsets, int64_t G, int64_t M_tot, int64_t N, int64_t K,

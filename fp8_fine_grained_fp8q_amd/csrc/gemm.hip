@@ -190,10 +190,14 @@ __device__ __forceinline__ bool grouped_tile(const int32_t *__restrict__ offsets
 // hold 256 rows of one 128-byte K block; narrower weight tiles leave the last rows unused.
 struct Stages {
   FP8Q_LDS uint8_t *x0, *w0, *x1, *w1;
+  FP8Q_LDS uint8_t *c0, *c1;  // per-column scales of the stage (row-scaled B operand only)
 };
 
-// Computes one 256 x 32*NFR tile of C.
-template <int NFR>
+// Computes one 256 x 32*NFR tile of C.  kRowB: the B operand (t.w) carries one scale per
+// row and 128-wide K block, t.sb[K/128][N] (a 1x128 tile quantized operand), instead of
+// one per 128x128 block; those scales ride along with each stage (1 KB through LDS) and the
+// promotion multiplies the two scales per element.
+template <int NFR, bool kRowB = false>
 __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict__ sa, int64_t M, int64_t N,
                                           int64_t K, void *__restrict__ c, int out_f32, const Stages &st) {
   constexpr int kBN = 32 * NFR;      // tile columns
@@ -230,8 +234,20 @@ __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict
   const int nb0 = static_cast<int>(min(static_cast<int64_t>(NB - 1), wc0 >> 7));
   const int nb1 = min(NB - 1, nb0 + 1);
   const int jsplit = static_cast<int>((128 - (wc0 & 127)) >> 4);
-  const float *sbrow0 = t.sb + static_cast<int64_t>(nb0) * KB;
-  const float *sbrow1 = t.sb + static_cast<int64_t>(nb1) * KB;
+  const float *sbrow0 = t.sb + static_cast<int64_t>(kRowB ? 0 : nb0) * KB;
+  const float *sbrow1 = t.sb + static_cast<int64_t>(kRowB ? 0 : nb1) * KB;
+  // Row-scaled B: the stage's column scales (lane l copies columns 4l .. 4l+3 of the
+  // tile).  Every wave issues the same 1 KB copy to the same LDS words: the writes are
+  // identical, and a branch here would split the loop body.  The buffer's range check
+  // counts the block's row offset (the scalar offset) too, so the resource spans the rest
+  // of the scale matrix; the copies past the tile's last column read other columns'
+  // finite scales, which only ever meet zero partials.
+  const __amdgpu_buffer_rsrc_t rsc = make_rsrc(t.sb + t.n0, static_cast<uint32_t>((KB * N - t.n0) * 4));
+  auto scale_load = [&](int kb, FP8Q_LDS uint8_t *dst) {
+    if (kRowB)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, (FP8Q_LDS void *)dst, 16, lane * 16,
+                                               static_cast<int>(kb * N * 4), 0, 0);
+  };
 
   v4f acc[4][NFR];
 #pragma unroll
@@ -244,10 +260,11 @@ __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict
 
   stage_load(rx, off, 0, st.x0, wave);
   stage_load<kWL>(rw, off, 0, st.w0, wave);
+  scale_load(0, st.c0);
 #pragma unroll
   for (int f = 0; f < 4; ++f) sa_cur[f] = sa[srow[f]];
-  sb0_cur = sbrow0[0];
-  sb1_cur = sbrow1[0];
+  sb0_cur = kRowB ? 0.0f : sbrow0[0];
+  sb1_cur = kRowB ? 0.0f : sbrow1[0];
 #pragma unroll
   for (int f = 0; f < 4; ++f) sa_nxt[f] = 0.0f;
 
@@ -259,13 +276,16 @@ __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict
   // body is branch-free (at the last block the copy just repeats that block).
   v4f pp[4];      // partials waiting to be folded
   float sclp[4];  // scales of the previous block's last column
+  float sa_prev[4];                          // row-scaled B: row scales of the previous block
+  v4f sbc_prev = v4f{0.0f, 0.0f, 0.0f, 0.0f};  // row-scaled B: scales of the column being folded
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
     pp[f] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     sclp[f] = 0.0f;
+    sa_prev[f] = 0.0f;
   }
   auto step = [&](const FP8Q_LDS uint8_t *cx, const FP8Q_LDS uint8_t *cw, FP8Q_LDS uint8_t *nx,
-                  FP8Q_LDS uint8_t *nw, int kb) {
+                  FP8Q_LDS uint8_t *nw, const FP8Q_LDS uint8_t *csc, FP8Q_LDS uint8_t *nsc, int kb) {
     // Stage kb has landed in LDS once every wave's own copies are done (vmcnt(0) before
     // the barrier: the compiler's fence does not count direct-to-LDS loads), and after
     // the barrier every wave is also done reading the other buffer.
@@ -280,11 +300,14 @@ __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict
     const uint32_t koff = static_cast<uint32_t>(kn) * kBK;
     stage_load(rx, off, koff, nx, wave);
     stage_load<kWL>(rw, off, koff, nw, wave);
+    scale_load(kn, nsc);
     const float *sak = sa + static_cast<int64_t>(kn) * M;
 #pragma unroll
     for (int f = 0; f < 4; ++f) sa_nxt[f] = sak[srow[f]];
-    sb0_nxt = sbrow0[kn];
-    sb1_nxt = sbrow1[kn];
+    if (!kRowB) {
+      sb0_nxt = sbrow0[kn];
+      sb1_nxt = sbrow1[kn];
+    }
 #pragma unroll
     for (int f = 1; f < 4; ++f) xf[f] = frag(cx, wm * 64 + f * 16 + l16, kg);
 #pragma unroll
@@ -302,20 +325,35 @@ __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict
 #pragma unroll
       for (int f = 0; f < 4; ++f) np[f] = mfma_block(wf, xf[f]);
       const int jp = j == 0 ? NFR - 1 : j - 1;
-      const float sbj = jp < jsplit ? sb0_cur : sb1_cur;  // wave-uniform
+      if constexpr (kRowB) {
+        // this column's four scales, folded with its partials at the next column
+        const v4f sbc_new = *reinterpret_cast<const FP8Q_LDS v4f *>(csc + (wn * kWN + j * 16 + 4 * kg) * 4);
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        const float sc = j == 0 ? sclp[f] : sa_cur[f] * sbj;
+        for (int f = 0; f < 4; ++f) {
+          const float sr = j == 0 ? sa_prev[f] : sa_cur[f];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[f][jp][i] = __builtin_fmaf(pp[f][i], sc, acc[f][jp][i]);
-        pp[f] = np[f];
+          for (int i = 0; i < 4; ++i) acc[f][jp][i] = __builtin_fmaf(pp[f][i] * sbc_prev[i], sr, acc[f][jp][i]);
+          pp[f] = np[f];
+        }
+        sbc_prev = sbc_new;
+      } else {
+        const float sbj = jp < jsplit ? sb0_cur : sb1_cur;  // wave-uniform
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const float sc = j == 0 ? sclp[f] : sa_cur[f] * sbj;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[f][jp][i] = __builtin_fmaf(pp[f][i], sc, acc[f][jp][i]);
+          pp[f] = np[f];
+        }
       }
       // Issue order within a column: each MFMA follows a group of promotion FMAs of the
       // previous column, so the vector ALU work sits between the matrix instructions.
+      if constexpr (!kRowB) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // 5 VALU
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+        for (int q = 0; q < 4; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // 5 VALU
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -323,6 +361,7 @@ __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       sclp[f] = sa_cur[f] * sbl;
+      sa_prev[f] = sa_cur[f];
       sa_cur[f] = sa_nxt[f];
     }
     sb0_cur = sb0_nxt;
@@ -331,15 +370,16 @@ __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict
 
   int kb = 0;
   for (; kb + 1 < KB; kb += 2) {
-    step(st.x0, st.w0, st.x1, st.w1, kb);
-    step(st.x1, st.w1, st.x0, st.w0, kb + 1);
+    step(st.x0, st.w0, st.x1, st.w1, st.c0, st.c1, kb);
+    step(st.x1, st.w1, st.x0, st.w0, st.c1, st.c0, kb + 1);
   }
-  if (kb < KB) step(st.x0, st.w0, st.x1, st.w1, kb);
+  if (kb < KB) step(st.x0, st.w0, st.x1, st.w1, st.c0, st.c1, kb);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the last (repeated) copy
 #pragma unroll
   for (int f = 0; f < 4; ++f)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[f][NFR - 1][i] = __builtin_fmaf(pp[f][i], sclp[f], acc[f][NFR - 1][i]);
+    for (int i = 0; i < 4; ++i)
+      acc[f][NFR - 1][i] = __builtin_fmaf(pp[f][i], kRowB ? sa_prev[f] * sbc_prev[i] : sclp[f], acc[f][NFR - 1][i]);
 
   // Epilogue: lane owns row m = m_begin + wm*64 + f*16 + l16 and columns
   // n0 + wn*kWN + j*16 + 4*kg + {0..3}.
@@ -371,13 +411,16 @@ __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict
   }
 }
 
-#define FP8Q_DECLARE_STAGES(st)                                          \
+#define FP8Q_DECLARE_STAGES(st, scale_bytes)                             \
   __shared__ __attribute__((aligned(1024))) uint8_t sx0[kBM * kBK];      \
   __shared__ __attribute__((aligned(1024))) uint8_t sw0[kBM * kBK];      \
   __shared__ __attribute__((aligned(1024))) uint8_t sx1[kBM * kBK];      \
   __shared__ __attribute__((aligned(1024))) uint8_t sw1[kBM * kBK];      \
+  __shared__ __attribute__((aligned(16))) uint8_t sc0[scale_bytes];      \
+  __shared__ __attribute__((aligned(16))) uint8_t sc1[scale_bytes];      \
   const Stages st = {(FP8Q_LDS uint8_t *)sx0, (FP8Q_LDS uint8_t *)sw0,   \
-                     (FP8Q_LDS uint8_t *)sx1, (FP8Q_LDS uint8_t *)sw1}
+                     (FP8Q_LDS uint8_t *)sx1, (FP8Q_LDS uint8_t *)sw1,   \
+                     (FP8Q_LDS uint8_t *)sc0, (FP8Q_LDS uint8_t *)sc1}
 
 // One tile width for the whole problem (dense: 1-D grid; grouped: see grouped_tile).
 template <int NFR, bool kGrouped>
@@ -385,7 +428,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(
     const uint8_t *__restrict__ xq, const float *__restrict__ sa, const uint8_t *__restrict__ wq,
     const float *__restrict__ sb, const int32_t *__restrict__ offsets, int G, int64_t M, int64_t N,
     int64_t K, void *__restrict__ c, int out_f32) {
-  FP8Q_DECLARE_STAGES(st);
+  FP8Q_DECLARE_STAGES(st, 16);
   Tile t;
   if (kGrouped) {
     if (!grouped_tile<32 * NFR>(offsets, G, M, N, K, wq, sb, t)) return;
@@ -406,7 +449,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_split_kernel(
     const uint8_t *__restrict__ xq, const float *__restrict__ sa, const uint8_t *__restrict__ wq,
     const float *__restrict__ sb, int64_t M, int64_t N, int64_t K, int64_t n_split, int tiles1,
     void *__restrict__ c, int out_f32) {
-  FP8Q_DECLARE_STAGES(st);
+  FP8Q_DECLARE_STAGES(st, 16);
   Tile t;
   const int bid = blockIdx.x;
   if (bid < tiles1) {
@@ -418,6 +461,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_split_kernel(
     t.x = xq;
     gemm_tile<NFR2>(t, sa, M, N, K, c, out_f32, st);
   }
+}
+
+// Both operands with per-row 1x128 scales (the weight-gradient GEMM dW = dY^T X over
+// token tiles): A = xq with sa[K/128][M], B = wq[N][K] with sb[K/128][N]; uniform tiles.
+template <int NFR>
+__global__ __launch_bounds__(kThreads, 1) void gemm_rowscaled_kernel(
+    const uint8_t *__restrict__ xq, const float *__restrict__ sa, const uint8_t *__restrict__ wq,
+    const float *__restrict__ sb, int64_t M, int64_t N, int64_t K, void *__restrict__ c, int out_f32) {
+  FP8Q_DECLARE_STAGES(st, 1024);
+  Tile t;
+  dense_tile<32 * NFR>(blockIdx.x, M, 0, N, wq, sb, t);
+  t.x = xq;
+  gemm_tile<NFR, true>(t, sa, M, N, K, c, out_f32, st);
 }
 
 namespace {
@@ -502,6 +558,19 @@ hipError_t launch_gemm(const uint8_t *xq, const float *sa, const uint8_t *wq, co
     hipLaunchKernelGGL((gemm_blockscaled_split_kernel<8, 6>), dim3(static_cast<uint32_t>(t1 + t2)), dim3(kThreads),
                        0, stream, xq, sa, wq, sb, M, N, K, best_a * 256, static_cast<int>(t1), c, out_f32 ? 1 : 0);
   }
+  return hipGetLastError();
+}
+
+#ifndef FP8Q_ROWSCALED_NFR
+#define FP8Q_ROWSCALED_NFR 8
+#endif
+hipError_t launch_gemm_rowscaled(const uint8_t *aq, const float *sa, const uint8_t *bq, const float *sb,
+                                 int64_t M, int64_t N, int64_t K, void *c, bool out_f32, hipStream_t stream) {
+  constexpr int NFR = FP8Q_ROWSCALED_NFR;
+  const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + 32 * NFR - 1) / (32 * NFR));
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_rowscaled_kernel<NFR>), dim3(static_cast<uint32_t>(tiles)), dim3(kThreads), 0, stream,
+                     aq, sa, bq, sb, M, N, K, c, out_f32 ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -110,12 +110,57 @@ hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, uint8_t *xq
 // t%16 of rows t/16 + 16*i, i = 0..7 (64 values in registers).  amax: DPP inside each
 // 16-lane row, readlane across the wave's four rows, LDS across the four waves.  The whole
 // block shares one scale, so the division path is uniform.
+//
+// With kTrans the block's codes are also written transposed (W^T[K][N] codes and the
+// block scale at [kb][nb]), the operand layout of the data-gradient GEMM dX = dY W: the
+// codes go through a 16 KB LDS tile and each thread turns four 4x4 byte squares around
+// with byte permutes, producing 16 consecutive N-bytes of four W^T rows.
 // ---------------------------------------------------------------------------------------
+
+// Byte transpose of a 4x4 square held as four dwords r0..r3 (row i = dword i, column j =
+// byte j): c[j] gets byte j of r0, r1, r2, r3 in bytes 0..3.  v_perm_b32 selects bytes
+// of {S0, S1} (selector 0..3 = S1 bytes 0..3, 4..7 = S0 bytes 0..3).
+__device__ __forceinline__ void transpose4x4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3, uint32_t c[4]) {
+  const uint32_t a = __builtin_amdgcn_perm(r1, r0, 0x06020400u);  // r0.b0 r1.b0 r0.b2 r1.b2
+  const uint32_t b = __builtin_amdgcn_perm(r1, r0, 0x07030501u);  // r0.b1 r1.b1 r0.b3 r1.b3
+  const uint32_t e = __builtin_amdgcn_perm(r3, r2, 0x06020400u);  // r2.b0 r3.b0 r2.b2 r3.b2
+  const uint32_t f = __builtin_amdgcn_perm(r3, r2, 0x07030501u);  // r2.b1 r3.b1 r2.b3 r3.b3
+  c[0] = __builtin_amdgcn_perm(e, a, 0x05040100u);
+  c[1] = __builtin_amdgcn_perm(f, b, 0x05040100u);
+  c[2] = __builtin_amdgcn_perm(e, a, 0x07060302u);
+  c[3] = __builtin_amdgcn_perm(f, b, 0x07060302u);
+}
+
+// Writes the transposed 128x128 code tile held in LDS (tile[row][col], 128-byte rows) as
+// rows of dst (row stride ld bytes): dst[col][row].  Thread t covers columns 4*(t%32)+j
+// (j < 4) and rows 16*(t/32) .. +15.
+__device__ __forceinline__ void store_transposed_tile(const uint32_t *tile, uint8_t *__restrict__ dst,
+                                                      int64_t ld, int tid) {
+  const int kd = tid & 31;
+  const int n0 = (tid >> 5) * 16;
+  uint32_t out[4][4];  // [column j][row group g]
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const uint32_t *p = tile + (n0 + 4 * g) * 32 + kd;
+    uint32_t c[4];
+    transpose4x4(p[0], p[32], p[64], p[96], c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j][g] = c[j];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    *reinterpret_cast<uint4 *>(dst + (4 * kd + j) * ld + n0) = make_uint4(out[j][0], out[j][1], out[j][2], out[j][3]);
+}
+
+template <bool kTrans>
 __global__ __launch_bounds__(256) void quant_w_128x128_kernel(const uint16_t *__restrict__ w,
                                                               int64_t N, int64_t K,
                                                               uint8_t *__restrict__ wq,
-                                                              float *__restrict__ sb) {
+                                                              float *__restrict__ sb,
+                                                              uint8_t *__restrict__ wqt,
+                                                              float *__restrict__ sbt) {
   __shared__ float wave_max[4];
+  __shared__ __attribute__((aligned(16))) uint32_t tile[kTrans ? 128 * 32 : 1];
   const int64_t KB = K >> 7, NB = N >> 7;
   const int64_t bid = blockIdx.x;
   const int64_t kb = bid % KB;
@@ -140,18 +185,159 @@ __global__ __launch_bounds__(256) void quant_w_128x128_kernel(const uint16_t *__
   const float s = amax / kE4M3Max;
   const GroupDiv dv(s);
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    *reinterpret_cast<uint2 *>(wq + base + (r0 + 16 * i) * K) = quant8(v[i], dv);
+  for (int i = 0; i < 8; ++i) {
+    const uint2 q = quant8(v[i], dv);
+    *reinterpret_cast<uint2 *>(wq + base + (r0 + 16 * i) * K) = q;
+    if (kTrans) *reinterpret_cast<uint2 *>(tile + (r0 + 16 * i) * 32 + sub * 2) = q;
+  }
   if (tid == 0) sb[gnb * KB + kb] = s;
-  (void)NB;
+  if (kTrans) {
+    const int64_t g = gnb / NB, nb = gnb % NB;
+    if (tid == 0) sbt[(g * KB + kb) * NB + nb] = s;
+    __syncthreads();
+    store_transposed_tile(tile, wqt + (g * K + kb * 128) * N + nb * 128, N, tid);
+  }
 }
 
 hipError_t launch_quant_w(const uint16_t *w, int64_t G, int64_t N, int64_t K, uint8_t *wq, float *sb,
-                          hipStream_t stream) {
+                          uint8_t *wqt, float *sbt, hipStream_t stream) {
   const int64_t blocks = G * (N / 128) * (K / 128);
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(quant_w_128x128_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
-                     stream, w, N, K, wq, sb);
+  if (wqt != nullptr)
+    hipLaunchKernelGGL(quant_w_128x128_kernel<true>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream,
+                       w, N, K, wq, sb, wqt, sbt);
+  else
+    hipLaunchKernelGGL(quant_w_128x128_kernel<false>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream,
+                       w, N, K, wq, sb, static_cast<uint8_t *>(nullptr), static_cast<float *>(nullptr));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// Activation quantizer in both orientations, for a layer whose input is needed by the
+// forward GEMM (tiles of 128 along K) and by the weight-gradient GEMM dW = dY^T X, whose
+// contraction runs over the tokens (tiles of 128 consecutive tokens of one channel, codes
+// stored channel-major as X^T[K][M]).  One 256-thread workgroup per 128x128 block of
+// X[M][K], the same register layout as the weight quantizer: thread t holds chunk t%16
+// (8 columns) of rows t/16 + 16*i.  Row tiles reduce inside a DPP row as in the 1x128
+// quantizer; column tiles reduce over the thread's 8 rows, across the wave with two
+// lane swaps and across the waves through LDS, where 128 threads also form the column
+// scales and reciprocals once.  The column codes are transposed through LDS like W^T.
+// The token count M must be a multiple of 128.
+// ---------------------------------------------------------------------------------------
+
+// y = RN32(x / s) for a divisor held as (s, r, mode) in the GroupDiv convention.
+__device__ __forceinline__ float div_any(float x, float s, float r, int mode) {
+  if (mode == 1) {
+    GroupDiv d(0.0f);
+    d.s = s;
+    d.r = r;
+    return d.fast(x);
+  }
+  return mode == 2 ? x / s : x;
+}
+
+__device__ __forceinline__ float bf16_elem(const uint4 &v, int e) {
+  const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+  return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+
+__global__ __launch_bounds__(256) void quant_act_dual_kernel(const uint16_t *__restrict__ x, int64_t M,
+                                                             int64_t K, uint8_t *__restrict__ xq,
+                                                             float *__restrict__ sa,
+                                                             uint8_t *__restrict__ xqt,
+                                                             float *__restrict__ sat) {
+  __shared__ float colmax[4][128];
+  __shared__ float colscale[128], colrcp[128];
+  __shared__ int colmode[128];
+  __shared__ __attribute__((aligned(16))) uint32_t tile[128 * 32];
+  const int64_t KB = K >> 7;
+  const int64_t kb = blockIdx.x % KB;
+  const int64_t mb = blockIdx.x / KB;
+  const int tid = threadIdx.x;
+  const int sub = tid & 15;
+  const int r0 = tid >> 4;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t base = (mb * 128) * K + kb * 128 + sub * 8;
+
+  uint4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = load16_stream(x + base + (r0 + 16 * i) * K);
+
+  // Row tiles (1x128 along K): the forward codes.
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float s = row16_max(absmax8(v[i])) / kE4M3Max;
+    *reinterpret_cast<uint2 *>(xq + base + (r0 + 16 * i) * K) = quant8(v[i], GroupDiv(s));
+    if (sub == 0) sa[kb * M + mb * 128 + r0 + 16 * i] = s;
+  }
+
+  // Column tiles (128 tokens of one channel).
+  float cm[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float m = fabsf(bf16_elem(v[0], e));
+#pragma unroll
+    for (int i = 1; i < 8; ++i) m = fmaxf(m, fabsf(bf16_elem(v[i], e)));
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    cm[e] = m;
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) colmax[wave][sub * 8 + e] = cm[e];
+  }
+  __syncthreads();
+  if (tid < 128) {
+    const float a = fmaxf(fmaxf(colmax[0][tid], colmax[1][tid]), fmaxf(colmax[2][tid], colmax[3][tid]));
+    const float s = a / kE4M3Max;
+    const GroupDiv d(s);
+    colscale[tid] = s;
+    colrcp[tid] = d.r;
+    colmode[tid] = d.mode;
+    sat[mb * K + kb * 128 + tid] = s;
+  }
+  __syncthreads();
+  float cs[8], cr[8];
+  int cmode[8];
+  bool all_fast = true;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    cs[e] = colscale[sub * 8 + e];
+    cr[e] = colrcp[sub * 8 + e];
+    cmode[e] = colmode[sub * 8 + e];
+    all_fast = all_fast && cmode[e] == 1;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float xv = bf16_elem(v[i], e);
+      if (all_fast) {
+        GroupDiv d(0.0f);
+        d.s = cs[e];
+        d.r = cr[e];
+        y[e] = d.fast(xv);
+      } else {
+        y[e] = div_any(xv, cs[e], cr[e], cmode[e]);
+      }
+    }
+    uint2 q;
+    q.x = pack4_e4m3(y[0], y[1], y[2], y[3]);
+    q.y = pack4_e4m3(y[4], y[5], y[6], y[7]);
+    *reinterpret_cast<uint2 *>(tile + (r0 + 16 * i) * 32 + sub * 2) = q;
+  }
+  __syncthreads();
+  store_transposed_tile(tile, xqt + (kb * 128) * M + mb * 128, M, tid);
+}
+
+hipError_t launch_quant_act_dual(const uint16_t *x, int64_t M, int64_t K, uint8_t *xq, float *sa,
+                                 uint8_t *xqt, float *sat, hipStream_t stream) {
+  const int64_t blocks = (M / 128) * (K / 128);
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_act_dual_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, x, M, K,
+                     xq, sa, xqt, sat);
   return hipGetLastError();
 }
 

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define FP8Q_ABI_VERSION 1
+#define FP8Q_ABI_VERSION 2
 
 typedef int32_t fp8q_status;
 
@@ -122,6 +122,61 @@ fp8q_status fp8q_grouped_gemm_blockscaled(const uint8_t *xq, const float *sa, co
                                           const float *sb, const int32_t *offsets, int64_t G,
                                           int64_t M_tot, int64_t N, int64_t K, void *c,
                                           int32_t out_dtype, void *stream);
+
+/*
+ * Backward pass of a linear layer Y = X W^T in the same E4M3 format.  Source: the
+ * codingmall.com page, section "Dinh dang E4M3 hop nhat", and the risenshineclean.com
+ * page, section 3, bullet on the unified E4M3 format (one FP8 format for the forward and
+ * the backward pass, made possible by the fine-grained groups); online scales as above.
+ * The pages give no formula for the backward GEMMs; these calls follow the plainest
+ * reading:
+ *  - dgrad dX = dY W: dY is quantized like any activation (fp8q_quantize_act_1x128, tiles
+ *    of 128 along N) and W keeps its forward 128x128 blocks, used transposed.  With the
+ *    W^T codes and scales from fp8q_quantize_w_128x128_t, dX is fp8q_gemm_blockscaled(dYq,
+ *    sa_dY, wqt, sbt, M, K, N, dX, ...).
+ *  - wgrad dW = dY^T X: the contraction runs over the tokens, so both operands are
+ *    quantized in tiles of 128 consecutive tokens of one channel (fp8q_quantize_act_dual)
+ *    and multiplied by fp8q_gemm_rowscaled(dYq^T, s_dY, Xq^T, s_X, N, K, M, dW, ...).
+ */
+
+/*
+ * Weight quantizer that also writes the transposed codes and scales, reading W once:
+ *   w_bf16, wq, sb : as in fp8q_quantize_w_128x128
+ *   wqt : [G][K][N] E4M3 codes of W^T (out): wqt[g][k][n] = wq[g][n][k]
+ *   sbt : [G][K/128][N/128] FP32 scales of W^T (out): sbt[g][kb][nb] = sb[g][nb][kb]
+ * Requires G >= 1, N % 128 == 0, K % 128 == 0.  N == 0 or K == 0 is a no-op.
+ * Errors: as fp8q_quantize_w_128x128; wqt and sbt are required (FP8Q_ERR_NULL).
+ */
+fp8q_status fp8q_quantize_w_128x128_t(const uint16_t *w_bf16, int64_t G, int64_t N, int64_t K,
+                                      uint8_t *wq, float *sb, uint8_t *wqt, float *sbt, void *stream);
+
+/*
+ * Activation quantizer in both orientations, reading X once:
+ *   x_bf16 : [M][K] BF16, row-major (M tokens, K channels)
+ *   xq, sa : 1x128 tiles along K, exactly as fp8q_quantize_act_1x128 writes them (out)
+ *   xqt    : [K][M] E4M3 codes of X^T, tiles of 128 consecutive tokens of one channel (out)
+ *   sat    : [M/128][K] FP32 scales of those tiles (out); sat[mb][k] belongs to tokens
+ *            128 mb .. 128 mb + 127 of channel k
+ * Requires M % 128 == 0 (pad the token dimension with zero rows), K % 128 == 0.
+ * M == 0 or K == 0 is a no-op.  Errors: FP8Q_ERR_SHAPE (M or K not a multiple of 128),
+ * FP8Q_ERR_NULL, FP8Q_ERR_ALIGN, FP8Q_ERR_DEVICE, FP8Q_ERR_LAUNCH.
+ */
+fp8q_status fp8q_quantize_act_dual(const uint16_t *x_bf16, int64_t M, int64_t K, uint8_t *xq,
+                                   float *sa, uint8_t *xqt, float *sat, void *stream);
+
+/*
+ * FP8 GEMM whose operands both carry 1x128 row-tile scales (the weight-gradient GEMM):
+ *   C[p][q] = sum_kb sa[kb][p] * sb[kb][q] * sum_{k in block kb} decode(aq[p][k]) decode(bq[q][k])
+ * with the same FP32 promotion per 128-wide K block as the block-scaled GEMM.
+ *   aq [P][Kc] codes, sa [Kc/128][P] FP32; bq [Q][Kc] codes, sb [Kc/128][Q] FP32
+ *   (for dW: aq = dY^T codes, bq = X^T codes, Kc = tokens, both from fp8q_quantize_act_dual)
+ *   c [P][Q] row-major, BF16 or FP32 per out_dtype (out)
+ * Requires Q % 128 == 0, Kc % 128 == 0, Kc >= 128, P >= 0, and (Kc/128) * Q * 4 < 2^31.
+ * Errors: as fp8q_gemm_blockscaled.
+ */
+fp8q_status fp8q_gemm_rowscaled(const uint8_t *aq, const float *sa, const uint8_t *bq, const float *sb,
+                                int64_t P, int64_t Q, int64_t Kc, void *c, int32_t out_dtype,
+                                void *stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *fp8q_status_string(fp8q_status status);

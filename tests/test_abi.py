@@ -97,6 +97,32 @@ def test_gemm_argument_checks(lib):
     assert gg(None, None, None, None, None, 2, 0, 128, 128, None, 0, None) == E["FP8Q_OK"]
 
 
+def test_backward_entry_point_argument_checks(lib):
+    E = header_enums()
+    A = ALIGNED
+    t = lib.fp8q_quantize_w_128x128_t
+    assert t(A, 1, 100, 128, A, A, A, A, None) == E["FP8Q_ERR_SHAPE"]
+    assert t(A, 0, 128, 128, A, A, A, A, None) == E["FP8Q_ERR_SHAPE"]
+    assert t(A, 1, 128, 128, A, A, None, A, None) == E["FP8Q_ERR_NULL"]
+    assert t(A, 1, 128, 128, A, A, A, None, None) == E["FP8Q_ERR_NULL"]
+    assert t(A, 1, 128, 128, A, A, A + 4, A, None) == E["FP8Q_ERR_ALIGN"]
+    assert t(None, 1, 0, 128, None, None, None, None, None) == E["FP8Q_OK"]
+    d = lib.fp8q_quantize_act_dual
+    assert d(A, 200, 128, A, A, A, A, None) == E["FP8Q_ERR_SHAPE"]   # tokens not a multiple of 128
+    assert d(A, 256, 100, A, A, A, A, None) == E["FP8Q_ERR_SHAPE"]
+    assert d(A, 256, 128, A, A, None, A, None) == E["FP8Q_ERR_NULL"]
+    assert d(A, 256, 128, A, A, A, A + 8, None) == E["FP8Q_ERR_ALIGN"]
+    assert d(None, 0, 128, None, None, None, None, None) == E["FP8Q_OK"]
+    r = lib.fp8q_gemm_rowscaled
+    assert r(A, A, A, A, 4, 128, 128, A, 5, None) == E["FP8Q_ERR_DTYPE"]
+    assert r(A, A, A, A, 4, 100, 128, A, 0, None) == E["FP8Q_ERR_SHAPE"]
+    assert r(A, A, A, A, 4, 128, 64, A, 0, None) == E["FP8Q_ERR_SHAPE"]
+    assert r(A, A, A, A, 4, 1 << 20, 1 << 17, A, 0, None) == E["FP8Q_ERR_SHAPE"]  # scale offsets too large
+    assert r(A, None, A, A, 4, 128, 128, A, 0, None) == E["FP8Q_ERR_NULL"]
+    assert r(A, A, A, A + 4, 4, 128, 128, A, 0, None) == E["FP8Q_ERR_ALIGN"]
+    assert r(None, None, None, None, 0, 128, 128, None, 0, None) == E["FP8Q_OK"]
+
+
 def test_valid_call_without_gpu_reports_device_error(lib):
     """On a host without a GPU a well-formed call must fail cleanly, not crash."""
     import torch

@@ -27,7 +27,7 @@ import os
 
 import numpy as np
 
-SEEDS = {"tiny": 1, "dense": 2, "moe_up": 3, "moe_down": 4, "large": 5}
+SEEDS = {"tiny": 1, "dense": 2, "moe_up": 3, "moe_down": 4, "large": 5, "train": 6}
 
 
 def bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -141,4 +141,17 @@ def large(seed: int = SEEDS["large"], M: int = 16384, N: int = 18432, K: int = 7
     return {"name": "large", "x": bf16_bits(x), "w": w, "offsets": None, "out_dtype": "f32"}
 
 
-CONFIGS = {"tiny": tiny, "dense": dense, "moe_up": moe_up, "moe_down": moe_down, "large": large}
+def train(seed: int = SEEDS["train"], M: int = 4096, N: int = 7168, K: int = 7168):
+    """One training step of the dense projection: the dense workload's X and W plus an
+    output gradient dY[M][N] (N(0,1) x 1e-3, with the rows of 16 tokens scaled x50 so the
+    token tiles see outliers too)."""
+    c = dense(M=M, N=N, K=K)
+    r_dy, r_tok = _rngs(seed, 2)
+    dy = r_dy.standard_normal((M, N), dtype=np.float32) * np.float32(1e-3)
+    tok = r_tok.choice(M, size=16, replace=False)
+    dy[tok] *= np.float32(50.0)
+    c.update({"name": "train", "dy": bf16_bits(dy), "out_dtype": "bf16"})
+    return c
+
+
+CONFIGS = {"tiny": tiny, "dense": dense, "moe_up": moe_up, "moe_down": moe_down, "large": large, "train": train}
