@@ -36,5 +36,6 @@ Modules:
     gemm   -- dequantized FP64 GEMM, dense and grouped, and the acceptance bound
     backward -- dgrad / wgrad of a linear layer: transposed weight blocks, 128x1
               token tiles, the GEMM with per-row scales on both operands
+    swiglu -- SwiGLU of the expert up-projection output followed by the 1x128 quantizer
 """
-from . import e4m3, quant, gemm, backward  # noqa: F401
+from . import e4m3, quant, gemm, backward, swiglu  # noqa: F401
