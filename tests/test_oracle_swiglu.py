@@ -27,7 +27,9 @@ def test_silu_identities():
     h_pos = swiglu.swiglu_f64(gu_of(g, ones))
     h_neg = swiglu.swiglu_f64(gu_of(-g, ones))
     np.testing.assert_allclose(h_pos - h_neg, gb, rtol=1e-13, atol=4e-15)
-    np.testing.assert_allclose(h_pos, gb / 2 * (1 + np.tanh(gb / 2)), rtol=1e-13, atol=1e-300)
+    # the tanh form cancels for very negative x, so compare where 1 + tanh(x/2) keeps its bits
+    keep = gb > -4
+    np.testing.assert_allclose(h_pos[keep], (gb / 2 * (1 + np.tanh(gb / 2)))[keep], rtol=1e-13)
 
 
 def test_silu_printed_values():
