@@ -9,8 +9,11 @@ One step = one pass of the whole path over one batch of synthetic input:
        grouped over experts for the MoE workloads.
 Default workload: the dense projection X[4096x7168] x W[7168x7168]^T, BF16 out.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense|large|moe_up|moe_down|train]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense|large|moe_up|moe_down|moe_ffn|train]
 
+The `moe_ffn` workload runs the expert FFN forward: activation and expert-weight
+quantization, the grouped up-projection, the fused SwiGLU + 1x128 quantizer, and the grouped
+down-projection; value = both GEMMs' FLOPs per step.
 The `train` workload runs one training step of the dense layer instead: both-orientation
 quantization of X and dY, the transposing weight quantizer, and the three GEMMs (forward,
 dgrad through the W^T blocks, wgrad over token tiles); value = 3*2*M*N*K FLOPs per step.
@@ -49,6 +52,8 @@ WORKLOADS = {
     "large": "large fused pipeline X[16384x7168] (Student-t 3) . W[18432x7168]^T, fp32 out",
     "moe_up": "MoE up-projection, 32 local experts of 256 (top-8 routing of 8192 tokens), W[32][4096x7168], bf16 out",
     "moe_down": "MoE down-projection, 32 local experts, SiLU(g)*u inputs [n x 2048], W[32][7168x2048], bf16 out",
+    "moe_ffn": "MoE expert FFN forward, 32 local experts (top-8 routing of 8192 tokens, 8360 rows): "
+               "X[8360x7168] -> up W[32][4096x7168] -> SwiGLU+quant -> down W[32][7168x2048], bf16 out",
     "train": "training step of the dense projection X[4096x7168], W[7168x7168]: forward Y = X W^T (bf16), "
              "dgrad dX = dY W (bf16), wgrad dW = dY^T X over the 4096 tokens (fp32)",
 }
@@ -133,6 +138,89 @@ def cpu_baseline(cfg, flops_step):
                   f"to {M} rows, weight quant x{G} experts")
     return {"value": flops_step / t_step / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": sample, "seconds_measured": round(t3 - t0, 2), "seconds_per_step_extrapolated": round(t_step, 2)}
+
+
+def run_moe_ffn(args, torch, fq, dev):
+    """The `moe_ffn` workload (see the module docstring)."""
+    cfg = gen("moe_ffn")
+    x_np, wu_np, wd_np, offsets = cfg["x"], cfg["w"], cfg["w_down"], cfg["offsets"]
+    M, K = x_np.shape
+    G, N1, _ = wu_np.shape
+    I = N1 // 2
+    flops = 2.0 * M * N1 * K + 2.0 * M * K * I
+    x0 = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    wu0 = torch.from_numpy(wu_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    wd0 = torch.from_numpy(wd_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    off_d = torch.from_numpy(offsets).to(dev)
+    per_set = 2 * (x0.numel() + wu0.numel() + wd0.numel()) * 2
+    nsets = min(8, args.sets or max(2, int(np.ceil(3 * 256e6 / per_set))))
+    u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
+    sets = []
+    for i in range(nsets):
+        sets.append({
+            "x": x0 if i == 0 else x0.clone(), "wu": wu0 if i == 0 else wu0.clone(), "wd": wd0 if i == 0 else wd0.clone(),
+            "xq": torch.empty((M, K), dtype=u8, device=dev), "sa": torch.empty((K // 128, M), dtype=f32, device=dev),
+            "wuq": torch.empty((G, N1, K), dtype=u8, device=dev), "sbu": torch.empty((G, N1 // 128, K // 128), dtype=f32, device=dev),
+            "wdq": torch.empty((G, K, I), dtype=u8, device=dev), "sbd": torch.empty((G, K // 128, I // 128), dtype=f32, device=dev),
+            "gu": torch.empty((M, N1), dtype=bf, device=dev),
+            "hq": torch.empty((M, I), dtype=u8, device=dev), "sh": torch.empty((I // 128, M), dtype=f32, device=dev),
+            "y": torch.empty((M, K), dtype=bf, device=dev),
+        })
+    stream = torch.cuda.current_stream()
+    names = ["quant_act(X)", "quant_w(W_up)", "grouped gemm up", "swiglu_quant(h)", "quant_w(W_down)",
+             "grouped gemm down"]
+
+    def step(s, ev=None):
+        calls = [
+            lambda: fq.fp8q_quantize_act_1x128(s["x"], xq=s["xq"], sa=s["sa"], stream=stream),
+            lambda: fq.fp8q_quantize_w_128x128(s["wu"], wq=s["wuq"], sb=s["sbu"], stream=stream),
+            lambda: fq.fp8q_grouped_gemm_blockscaled(s["xq"], s["sa"], s["wuq"], s["sbu"], off_d, out=s["gu"],
+                                                     stream=stream),
+            lambda: fq.fp8q_swiglu_quantize_act_1x128(s["gu"], xq=s["hq"], sa=s["sh"], stream=stream),
+            lambda: fq.fp8q_quantize_w_128x128(s["wd"], wq=s["wdq"], sb=s["sbd"], stream=stream),
+            lambda: fq.fp8q_grouped_gemm_blockscaled(s["hq"], s["sh"], s["wdq"], s["sbd"], off_d, out=s["y"],
+                                                     stream=stream),
+        ]
+        for i, c in enumerate(calls):
+            if ev is not None:
+                ev[i].record(stream)
+            c()
+        if ev is not None:
+            ev[len(calls)].record(stream)
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % nsets], evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)])) * 1e3
+           for j, n in enumerate(names)}
+    gflops = {"grouped gemm up": 2.0 * M * N1 * K, "grouped gemm down": 2.0 * M * K * I}
+    tflops = {n: round(f / (per[n] * 1e-6) / 1e12, 1) for n, f in gflops.items()}
+    dom = max(gflops, key=lambda n: per[n])
+    h_bytes = M * N1 * 2 + M * I + 4 * M * (I // 128)
+    value = flops * args.steps / wall / 1e12
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic (seeded; shapes and distributions of the workload, no dataset)",
+        "config": {"workload": WORKLOADS["moe_ffn"], "M": M, "hidden": K, "intermediate": I, "experts": G,
+                   "buffer_sets": nsets},
+        "pct_fp8_peak_step": round(value / PEAK_FP8_TFLOPS * 100, 2),
+        "kernels_us": {n: round(v, 2) for n, v in per.items()},
+        "gemm_tflops": tflops,
+        "swiglu_quant_GBs": round(h_bytes / (per["swiglu_quant(h)"] * 1e-6) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": tflops[dom], "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops[dom] / PEAK_FP8_TFLOPS, 4), "traffic": None, "kernel": dom,
+                     "flop_per_launch": gflops[dom], "avg_launch_us": round(per[dom], 2)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
 
 
 def run_train(args, torch, fq, dev):
@@ -226,8 +314,8 @@ def main():
         sys.exit(1)
     fq.load_library()
     dev = torch.device("cuda:0")
-    if args.workload == "train":
-        run_train(args, torch, fq, dev)
+    if args.workload in ("train", "moe_ffn"):
+        (run_train if args.workload == "train" else run_moe_ffn)(args, torch, fq, dev)
         return
 
     t_gen = time.perf_counter()

@@ -34,11 +34,12 @@ LIB_PATH = os.environ.get("FP8Q_LIBRARY") or os.path.join(HERE, "libfp8q.so")
 FP8Q_OK = 0
 FP8Q_OUT_BF16 = 0
 FP8Q_OUT_F32 = 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 EXPORTED = ("fp8q_quantize_act_1x128", "fp8q_quantize_w_128x128", "fp8q_gemm_blockscaled",
             "fp8q_grouped_gemm_blockscaled", "fp8q_quantize_w_128x128_t", "fp8q_quantize_act_dual",
-            "fp8q_gemm_rowscaled", "fp8q_status_string", "fp8q_abi_version")
+            "fp8q_gemm_rowscaled", "fp8q_swiglu_quantize_act_1x128", "fp8q_status_string",
+            "fp8q_abi_version")
 
 
 class Fp8qError(RuntimeError):
@@ -67,9 +68,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp8q_quantize_w_128x128_t.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp]
     lib.fp8q_quantize_act_dual.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
     lib.fp8q_gemm_rowscaled.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i32, vp]
+    lib.fp8q_swiglu_quantize_act_1x128.argtypes = [vp, i64, i64, vp, vp, vp]
     for name in ("fp8q_quantize_act_1x128", "fp8q_quantize_w_128x128", "fp8q_gemm_blockscaled",
                  "fp8q_grouped_gemm_blockscaled", "fp8q_quantize_w_128x128_t", "fp8q_quantize_act_dual",
-                 "fp8q_gemm_rowscaled"):
+                 "fp8q_gemm_rowscaled", "fp8q_swiglu_quantize_act_1x128"):
         getattr(lib, name).restype = i32
     lib.fp8q_status_string.argtypes = [i32]
     lib.fp8q_status_string.restype = ctypes.c_char_p
@@ -228,6 +230,18 @@ def fp8q_gemm_rowscaled(aq, sa, bq, sb, out_dtype=torch.bfloat16, out: torch.Ten
     return out
 
 
+def fp8q_swiglu_quantize_act_1x128(gu: torch.Tensor, xq=None, sa=None, stream=None):
+    """gu bf16 [M, 2I] (g | u) -> (xq uint8 [M, I], sa float32 [I/128, M]) for h = SiLU(g) * u."""
+    _need(gu, torch.bfloat16, "gu")
+    M, I2 = gu.shape
+    I = I2 // 2
+    xq = torch.empty((M, I), dtype=torch.uint8, device=gu.device) if xq is None else xq
+    sa = torch.empty((I // 128, M), dtype=torch.float32, device=gu.device) if sa is None else sa
+    _check(load_library().fp8q_swiglu_quantize_act_1x128(_ptr(gu), M, I, _ptr(xq), _ptr(sa), _stream(stream)),
+           "fp8q_swiglu_quantize_act_1x128")
+    return xq, sa
+
+
 quantize_act_1x128 = fp8q_quantize_act_1x128
 quantize_w_128x128 = fp8q_quantize_w_128x128
 gemm_blockscaled = fp8q_gemm_blockscaled
@@ -235,3 +249,4 @@ grouped_gemm_blockscaled = fp8q_grouped_gemm_blockscaled
 quantize_w_128x128_t = fp8q_quantize_w_128x128_t
 quantize_act_dual = fp8q_quantize_act_dual
 gemm_rowscaled = fp8q_gemm_rowscaled
+swiglu_quantize_act_1x128 = fp8q_swiglu_quantize_act_1x128

@@ -128,6 +128,16 @@ fp8q_status fp8q_gemm_rowscaled(const uint8_t *aq, const float *sa, const uint8_
                                               as_stream(stream)));
 }
 
+fp8q_status fp8q_swiglu_quantize_act_1x128(const uint16_t *gu_bf16, int64_t M, int64_t I, uint8_t *xq,
+                                           float *sa, void *stream) {
+  if (bad_dim(M) || bad_dim(I) || I % 128 != 0 || too_many(M, 2 * I)) return FP8Q_ERR_SHAPE;
+  if (M == 0 || I == 0) return FP8Q_OK;
+  if (!gu_bf16 || !xq || !sa) return FP8Q_ERR_NULL;
+  if (misaligned(gu_bf16) || misaligned(xq) || misaligned(sa)) return FP8Q_ERR_ALIGN;
+  if (device_ok() != FP8Q_OK) return FP8Q_ERR_DEVICE;
+  return launched(fp8q::launch_swiglu_quant_act(gu_bf16, M, I, xq, sa, as_stream(stream)));
+}
+
 const char *fp8q_status_string(fp8q_status status) {
   switch (status) {
     case FP8Q_OK: return "ok";

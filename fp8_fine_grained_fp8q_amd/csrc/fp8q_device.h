@@ -108,6 +108,25 @@ __device__ __forceinline__ uint2 quant8(const uint4 v, const GroupDiv &dv) {
   return out;
 }
 
+// Eight FP32 values -> eight E4M3 codes with divisor `dv` (as quant8, for values that are
+// not BF16 inputs, e.g. a fused producer's FP32 output).
+__device__ __forceinline__ uint2 quant8f(const float (&x)[8], const GroupDiv &dv) {
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = x[i];
+  if (dv.mode == 1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = dv.fast(y[i]);
+  } else if (dv.mode == 2) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = y[i] / dv.s;
+  }
+  uint2 out;
+  out.x = pack4_e4m3(y[0], y[1], y[2], y[3]);
+  out.y = pack4_e4m3(y[4], y[5], y[6], y[7]);
+  return out;
+}
+
 // Largest |x| of the eight BF16 values in a 16-byte chunk.
 __device__ __forceinline__ float absmax8(const uint4 v) {
   float m = fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x)));

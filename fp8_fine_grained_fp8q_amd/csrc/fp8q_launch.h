@@ -19,6 +19,10 @@ hipError_t launch_quant_w(const uint16_t *w, int64_t G, int64_t N, int64_t K, ui
 hipError_t launch_quant_act_dual(const uint16_t *x, int64_t M, int64_t K, uint8_t *xq, float *sa,
                                  uint8_t *xqt, float *sat, hipStream_t stream);
 
+// h = SiLU(g) * u of gu[M][2I] (g left half, u right half), quantized in 1x128 tiles.
+hipError_t launch_swiglu_quant_act(const uint16_t *gu, int64_t M, int64_t I, uint8_t *xq, float *sa,
+                                   hipStream_t stream);
+
 hipError_t launch_gemm(const uint8_t *xq, const float *sa, const uint8_t *wq, const float *sb,
                        int64_t M, int64_t N, int64_t K, void *c, bool out_f32, hipStream_t stream);
 

@@ -341,4 +341,86 @@ hipError_t launch_quant_act_dual(const uint16_t *x, int64_t M, int64_t K, uint8_
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------------
+// SwiGLU + 1x128 activation quantizer (the MoE expert down-projection's input): reads the
+// up-projection output gu[M][2I] (g = columns 0..I-1, u = I..2I-1) once and writes the
+// E4M3 codes of h = SiLU(g) * u, h formed in FP32 (no BF16 round trip), with one online
+// scale per 1x128 tile of h.  Same slab layout as the activation quantizer: one wave
+// handles 4*NR rows x NK tiles, a tile is one 16-lane DPP row, 16 bytes of g and 16 of u
+// per lane.  SiLU(g) = g * sigma(g), sigma from e^-|g| (the library exponential, about one
+// ulp; no overflow for any g) and the hardware reciprocal (one ulp).  Values of h below the
+// FP32 normal range (|h| < 2^-126) carry the subnormal rounding of the intermediate products.
+// ---------------------------------------------------------------------------------------
+template <int NR, int NK>
+__global__ __launch_bounds__(256) void swiglu_quant_act_1x128_kernel(const uint16_t *__restrict__ gu,
+                                                                     int64_t M, int64_t I,
+                                                                     uint8_t *__restrict__ xq,
+                                                                     float *__restrict__ sa) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = static_cast<int64_t>(blockIdx.x) * kActWavesPerBlock + (threadIdx.x >> 6);
+  const int64_t KB = I >> 7;
+  const int64_t KG = (KB + NK - 1) / NK;
+  const int64_t kb0 = (wave % KG) * NK;
+  const int64_t row0 = (wave / KG) * (4 * NR);
+  if (row0 >= M) return;
+  const int grp = lane >> 4;
+  const int sub = lane & 15;
+  const int64_t ld = 2 * I;
+
+  uint4 vg[NK][NR], vu[NK][NR];
+#pragma unroll
+  for (int k = 0; k < NK; ++k)
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int64_t row = row0 + 4 * i + grp;
+      const int64_t col = (kb0 + k) * 128 + sub * 8;
+      if (row < M && kb0 + k < KB) {
+        vg[k][i] = load16_stream(gu + row * ld + col);
+        vu[k][i] = load16_stream(gu + row * ld + I + col);
+      } else {
+        vg[k][i] = make_uint4(0u, 0u, 0u, 0u);
+        vu[k][i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    if (kb0 + k >= KB) break;
+    const int64_t col = (kb0 + k) * 128 + sub * 8;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const uint32_t gw[4] = {vg[k][i].x, vg[k][i].y, vg[k][i].z, vg[k][i].w};
+      const uint32_t uw[4] = {vu[k][i].x, vu[k][i].y, vu[k][i].z, vu[k][i].w};
+      float h[8];
+      float m = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float g = (e & 1) ? bf16_hi(gw[e >> 1]) : bf16_lo(gw[e >> 1]);
+        const float u = (e & 1) ? bf16_hi(uw[e >> 1]) : bf16_lo(uw[e >> 1]);
+        // sigma(g) = 1 / (1 + e^-g) for g >= 0 and e^g / (1 + e^g) for g < 0: e^-|g| never
+        // overflows
+        const float t = expf(-fabsf(g));
+        h[e] = g * u * ((g >= 0.0f ? 1.0f : t) * __builtin_amdgcn_rcpf(1.0f + t));
+        m = fmaxf(m, fabsf(h[e]));
+      }
+      const float s = row16_max(m) / kE4M3Max;
+      const int64_t row = row0 + 4 * i + grp;
+      const uint2 q = quant8f(h, GroupDiv(s));
+      if (row < M) *reinterpret_cast<uint2 *>(xq + row * I + col) = q;
+      if (sub == 0 && row < M) sa[(kb0 + k) * M + row] = s;
+    }
+  }
+}
+
+hipError_t launch_swiglu_quant_act(const uint16_t *gu, int64_t M, int64_t I, uint8_t *xq, float *sa,
+                                   hipStream_t stream) {
+  constexpr int NR = 2, NK = 2;
+  const int64_t KB = I / 128;
+  const int64_t waves = ((M + 4 * NR - 1) / (4 * NR)) * ((KB + NK - 1) / NK);
+  const int64_t blocks = (waves + kActWavesPerBlock - 1) / kActWavesPerBlock;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((swiglu_quant_act_1x128_kernel<NR, NK>), dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                     stream, gu, M, I, xq, sa);
+  return hipGetLastError();
+}
+
 }  // namespace fp8q

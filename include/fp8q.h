@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define FP8Q_ABI_VERSION 2
+#define FP8Q_ABI_VERSION 3
 
 typedef int32_t fp8q_status;
 
@@ -177,6 +177,24 @@ fp8q_status fp8q_quantize_act_dual(const uint16_t *x_bf16, int64_t M, int64_t K,
 fp8q_status fp8q_gemm_rowscaled(const uint8_t *aq, const float *sa, const uint8_t *bq, const float *sb,
                                 int64_t P, int64_t Q, int64_t Kc, void *c, int32_t out_dtype,
                                 void *stream);
+
+/*
+ * SwiGLU of an expert up-projection output followed by the 1x128 activation quantizer, in
+ * one pass (the input of the MoE down-projection GEMM).  Source: the MoE expert FFN
+ * (risenshineclean.com page, section 2) and the online 1x128 quantization of every GEMM
+ * activation (codingmall.com page, sections "Dinh luong hat min", "Dinh luong truc
+ * tuyen").  The pages do not name the activation; SwiGLU h = SiLU(g) * u is the reading.
+ *   gu_bf16 : [M][2I] BF16 row-major; g = columns 0..I-1, u = columns I..2I-1
+ *   xq      : [M][I] E4M3 codes of h (out), h formed in FP32 from the BF16 g and u
+ *   sa      : [I/128][M] FP32 tile scales of h (out)
+ * SiLU(g) = g / (1 + e^-g) is computed in FP32 with about two ulps of error, so codes can
+ * differ from a correctly rounded h where h / s lies within a few ulps of an E4M3
+ * rounding boundary; values of h below the FP32 normal range (|h| < 2^-126, e.g. gates
+ * below -87) are not reproduced to that accuracy.  Requires I % 128 == 0, M >= 0.
+ * Errors as the activation quantizer.
+ */
+fp8q_status fp8q_swiglu_quantize_act_1x128(const uint16_t *gu_bf16, int64_t M, int64_t I, uint8_t *xq,
+                                           float *sa, void *stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *fp8q_status_string(fp8q_status status);

@@ -123,6 +123,18 @@ def test_backward_entry_point_argument_checks(lib):
     assert r(None, None, None, None, 0, 128, 128, None, 0, None) == E["FP8Q_OK"]
 
 
+def test_swiglu_quantizer_argument_checks(lib):
+    E = header_enums()
+    A = ALIGNED
+    f = lib.fp8q_swiglu_quantize_act_1x128
+    assert f(A, 4, 100, A, A, None) == E["FP8Q_ERR_SHAPE"]
+    assert f(A, -1, 128, A, A, None) == E["FP8Q_ERR_SHAPE"]
+    assert f(None, 4, 128, A, A, None) == E["FP8Q_ERR_NULL"]
+    assert f(A, 4, 128, A, None, None) == E["FP8Q_ERR_NULL"]
+    assert f(A + 2, 4, 128, A, A, None) == E["FP8Q_ERR_ALIGN"]
+    assert f(None, 0, 128, None, None, None) == E["FP8Q_OK"]
+
+
 def test_valid_call_without_gpu_reports_device_error(lib):
     """On a host without a GPU a well-formed call must fail cleanly, not crash."""
     import torch

@@ -141,6 +141,16 @@ def large(seed: int = SEEDS["large"], M: int = 16384, N: int = 18432, K: int = 7
     return {"name": "large", "x": bf16_bits(x), "w": w, "offsets": None, "out_dtype": "f32"}
 
 
+def moe_ffn(seed: int = SEEDS["moe_up"]):
+    """The expert FFN forward of the 32 local experts: the moe_up input and up-projection
+    weights plus the moe_down workload's down-projection weights W_down[32][7168x2048]."""
+    up = moe_up(seed)
+    G, N1, K = up["w"].shape
+    w_down = _weights(_rngs(SEEDS["moe_down"] * 1000 + 7, G), G, K, N1 // 2)
+    return {"name": "moe_ffn", "x": up["x"], "w": up["w"], "w_down": w_down, "offsets": up["offsets"],
+            "out_dtype": "bf16"}
+
+
 def train(seed: int = SEEDS["train"], M: int = 4096, N: int = 7168, K: int = 7168):
     """One training step of the dense projection: the dense workload's X and W plus an
     output gradient dY[M][N] (N(0,1) x 1e-3, with the rows of 16 tokens scaled x50 so the
@@ -154,4 +164,5 @@ def train(seed: int = SEEDS["train"], M: int = 4096, N: int = 7168, K: int = 716
     return c
 
 
-CONFIGS = {"tiny": tiny, "dense": dense, "moe_up": moe_up, "moe_down": moe_down, "large": large, "train": train}
+CONFIGS = {"tiny": tiny, "dense": dense, "moe_up": moe_up, "moe_down": moe_down, "large": large, "train": train,
+           "moe_ffn": moe_ffn}
