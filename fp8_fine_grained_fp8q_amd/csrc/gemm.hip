@@ -71,11 +71,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
 // c = 8*i + w (8 rows each, 1 KB); lane p of chunk c lands at LDS row 8c + p/8, slot p%8,
 // and fetches global chunk slot ^ swz(row) of that row.  Both operands use these offsets
 // (both have row stride K).
-__device__ __forceinline__ void stage_offsets(int64_t K, int wave, int lane, uint32_t off[4]) {
+template <int NO = 4>
+__device__ __forceinline__ void stage_offsets(int64_t K, int wave, int lane, uint32_t (&off)[NO]) {
   const int r_in = lane >> 3;
   const int slot = lane & 7;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NO; ++i) {
     const int row = 8 * (8 * i + wave) + r_in;
     off[i] = static_cast<uint32_t>(row) * static_cast<uint32_t>(K) + static_cast<uint32_t>((slot ^ swz(row)) << 4);
   }
@@ -86,7 +87,7 @@ __device__ __forceinline__ void stage_offsets(int64_t K, int wave, int lane, uin
 // buffer bounds check without touching memory, so every wave always issues NL loads and
 // the loop body stays free of branches.
 template <int NL = 4>
-__device__ __forceinline__ void stage_load(__amdgpu_buffer_rsrc_t rsrc, const uint32_t off[4], uint32_t koff,
+__device__ __forceinline__ void stage_load(__amdgpu_buffer_rsrc_t rsrc, const uint32_t *off, uint32_t koff,
                                            FP8Q_LDS uint8_t *lds, int wave) {
 #pragma unroll
   for (int i = 0; i < NL; ++i)
@@ -157,35 +158,6 @@ __device__ __forceinline__ void dense_tile(int bid, int64_t M, int64_t n_lo, int
   t.sb = sb;
 }
 
-// Grouped: blockIdx.y is the N tile, blockIdx.x enumerates the M tiles of all experts in
-// order (expert g contributes ceil(n_g / 256) tiles).  Offsets come from device memory;
-// every range is clamped to [0, M_tot).
-template <int kBN>
-__device__ __forceinline__ bool grouped_tile(const int32_t *__restrict__ offsets, int G, int64_t M_tot,
-                                             int64_t N, int64_t K, const uint8_t *wq, const float *sb,
-                                             Tile &t) {
-  const int slot = blockIdx.x;
-  int cum = 0;
-  for (int g = 0; g < G; ++g) {
-    int64_t a = offsets[g], b = offsets[g + 1];
-    a = a < 0 ? 0 : (a > M_tot ? M_tot : a);
-    b = b < a ? a : (b > M_tot ? M_tot : b);
-    const int tiles = static_cast<int>((b - a + kBM - 1) / kBM);
-    if (slot < cum + tiles) {
-      const int64_t lo = a + static_cast<int64_t>(slot - cum) * kBM;
-      t.m_begin = lo;
-      t.rows = static_cast<int>(min(static_cast<int64_t>(kBM), b - lo));
-      t.n0 = static_cast<int64_t>(blockIdx.y) * kBN;
-      t.n_end = N;
-      t.w = wq + static_cast<int64_t>(g) * N * K;
-      t.sb = sb + static_cast<int64_t>(g) * (N / 128) * (K / 128);
-      return true;
-    }
-    cum += tiles;
-  }
-  return false;
-}
-
 // The LDS stages of one workgroup: activation and weight tiles, double buffered.  Both
 // hold 256 rows of one 128-byte K block; narrower weight tiles leave the last rows unused.
 struct Stages {
@@ -193,22 +165,26 @@ struct Stages {
   FP8Q_LDS uint8_t *c0, *c1;  // per-column scales of the stage (row-scaled B operand only)
 };
 
-// Computes one 256 x 32*NFR tile of C.  kRowB: the B operand (t.w) carries one scale per
-// row and 128-wide K block, t.sb[K/128][N] (a 1x128 tile quantized operand), instead of
-// one per 128x128 block; those scales ride along with each stage (1 KB through LDS) and the
-// promotion multiplies the two scales per element.
-template <int NFR, bool kRowB = false>
+// Computes one (64*WM) x (16*NFR*WN) tile of C, WM x WN = 8 waves (4 x 2: 256 x 32*NFR;
+// 2 x 4: 128 x 64*NFR), each wave 64 rows x 16*NFR columns.  kRowB: the B operand (t.w)
+// carries one scale per row and 128-wide K block, t.sb[K/128][N] (a 1x128 tile quantized
+// operand), instead of one per 128x128 block; those scales ride along with each stage
+// (1 KB through LDS) and the promotion multiplies the two scales per element.
+template <int NFR, bool kRowB = false, int WM = 4>
 __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict__ sa, int64_t M, int64_t N,
                                           int64_t K, void *__restrict__ c, int out_f32, const Stages &st) {
-  constexpr int kBN = 32 * NFR;      // tile columns
-  constexpr int kWN = 16 * NFR;      // columns per wave
+  constexpr int WN = 8 / WM;
+  constexpr int kBN = 16 * NFR * WN;  // tile columns
+  constexpr int kWN = 16 * NFR;       // columns per wave
+  constexpr int kXL = WM;             // activation-stage loads per wave (64*WM rows)
   constexpr int kWL = kBN % 64 == 0 ? kBN / 64 : 4;  // weight-stage loads per wave
+  constexpr int kNO = kWL > kXL ? kWL : kXL;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1;  // 0..3: rows wm*64 .. +63
-  const int wn = wave & 1;   // 0..1: cols wn*kWN .. +kWN-1
+  const int wm = wave / WN;  // rows wm*64 .. +63
+  const int wn = wave % WN;  // cols wn*kWN .. +kWN-1
   const int KB = static_cast<int>(K >> 7);
   const int NB = static_cast<int>(N >> 7);
   const int l16 = lane & 15;
@@ -218,7 +194,7 @@ __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(t.x + t.m_begin * K, static_cast<uint32_t>(t.rows * K));
   const int rows_w = static_cast<int>(min(static_cast<int64_t>(kBN), t.n_end - t.n0));
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(t.w + t.n0 * K, static_cast<uint32_t>(rows_w * K));
-  uint32_t off[4];
+  uint32_t off[kNO];
   stage_offsets(K, wave, lane, off);
 
   // activation-scale rows of this lane (one per 16-row fragment), clamped into the tile
@@ -258,7 +234,7 @@ __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict
   float sa_cur[4], sa_nxt[4];
   float sb0_cur, sb1_cur, sb0_nxt = 0.0f, sb1_nxt = 0.0f;
 
-  stage_load(rx, off, 0, st.x0, wave);
+  stage_load<kXL>(rx, off, 0, st.x0, wave);
   stage_load<kWL>(rw, off, 0, st.w0, wave);
   scale_load(0, st.c0);
 #pragma unroll
@@ -298,7 +274,7 @@ __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict
     xf[0] = frag(cx, wm * 64 + l16, kg);
     const int kn = kb + 1 < KB ? kb + 1 : kb;
     const uint32_t koff = static_cast<uint32_t>(kn) * kBK;
-    stage_load(rx, off, koff, nx, wave);
+    stage_load<kXL>(rx, off, koff, nx, wave);
     stage_load<kWL>(rw, off, koff, nw, wave);
     scale_load(kn, nsc);
     const float *sak = sa + static_cast<int64_t>(kn) * M;
@@ -422,19 +398,14 @@ __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict
                      (FP8Q_LDS uint8_t *)sx1, (FP8Q_LDS uint8_t *)sw1,   \
                      (FP8Q_LDS uint8_t *)sc0, (FP8Q_LDS uint8_t *)sc1}
 
-// One tile width for the whole problem (dense: 1-D grid; grouped: see grouped_tile).
-template <int NFR, bool kGrouped>
+// Dense problem, one tile width throughout (1-D grid).
+template <int NFR>
 __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(
     const uint8_t *__restrict__ xq, const float *__restrict__ sa, const uint8_t *__restrict__ wq,
-    const float *__restrict__ sb, const int32_t *__restrict__ offsets, int G, int64_t M, int64_t N,
-    int64_t K, void *__restrict__ c, int out_f32) {
+    const float *__restrict__ sb, int64_t M, int64_t N, int64_t K, void *__restrict__ c, int out_f32) {
   FP8Q_DECLARE_STAGES(st, 16);
   Tile t;
-  if (kGrouped) {
-    if (!grouped_tile<32 * NFR>(offsets, G, M, N, K, wq, sb, t)) return;
-  } else {
-    dense_tile<32 * NFR>(blockIdx.x, M, 0, N, wq, sb, t);
-  }
+  dense_tile<32 * NFR>(blockIdx.x, M, 0, N, wq, sb, t);
   t.x = xq;
   gemm_tile<NFR>(t, sa, M, N, K, c, out_f32, st);
 }
@@ -460,6 +431,95 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_split_kernel(
     dense_tile<32 * NFR2>(bid - tiles1, M, n_split, N, wq, sb, t);
     t.x = xq;
     gemm_tile<NFR2>(t, sa, M, N, K, c, out_f32, st);
+  }
+}
+
+// Grouped GEMM work items.  Expert g (rows offsets[g] .. offsets[g+1]-1, clamped to
+// [0, M_tot)) is cut into floor(n_g / 256) full 256-row tiles, each covering N in 256-wide
+// tiles, plus its tail of n_g mod 256 rows: a tail of at most 128 rows uses 128 x 512 tiles
+// (the same per-wave work, half as many tiles as 256 x 256 ones would need), a longer tail
+// one more row of 256 x 256 tiles.  Items are numbered expert by expert, N tile by N tile,
+// M tile last (tiles of one expert sharing a weight panel are adjacent), and workgroups are
+// dealt to the 8 XCDs in contiguous runs of items.  Returns the tile shape (0: 256 x 256,
+// 1: 128 x 512) or -1 past the last item.
+__device__ __forceinline__ int grouped_item(const int32_t *__restrict__ offsets, int G, int64_t M_tot, int64_t N,
+                                            int64_t K, const uint8_t *wq, const float *sb, Tile &t) {
+  const int nt_a = static_cast<int>((N + 255) / 256);
+  const int nt_b = static_cast<int>((N + 511) / 512);
+  auto range = [&](int g, int64_t &a, int64_t &b) {
+    a = offsets[g];
+    b = offsets[g + 1];
+    a = a < 0 ? 0 : (a > M_tot ? M_tot : a);
+    b = b < a ? a : (b > M_tot ? M_tot : b);
+  };
+  auto items_of = [&](int64_t n) {
+    const int64_t full = n / 256, tail = n % 256;
+    return full * nt_a + (tail == 0 ? 0 : (tail <= 128 ? nt_b : nt_a));
+  };
+  int64_t total = 0;
+  for (int g = 0; g < G; ++g) {
+    int64_t a, b;
+    range(g, a, b);
+    total += items_of(b - a);
+  }
+  const int64_t bid = blockIdx.x;
+  if (bid >= total) return -1;
+  const int64_t per = total / 8, rem = total % 8;
+  const int64_t xcd = bid % 8, idx = bid / 8;
+  int64_t item = xcd * per + (xcd < rem ? xcd : rem) + idx;
+  for (int g = 0; g < G; ++g) {
+    int64_t a, b;
+    range(g, a, b);
+    const int64_t n = b - a, cnt = items_of(n);
+    if (item >= cnt) {
+      item -= cnt;
+      continue;
+    }
+    t.w = wq + static_cast<int64_t>(g) * N * K;
+    t.sb = sb + static_cast<int64_t>(g) * (N / 128) * (K / 128);
+    t.n_end = N;
+    const int64_t full = n / 256;
+    if (item < full * nt_a) {
+      const int64_t nt = item / full, mt = item % full;
+      t.m_begin = a + mt * 256;
+      t.rows = 256;
+      t.n0 = nt * 256;
+      return 0;
+    }
+    item -= full * nt_a;
+    t.m_begin = a + full * 256;
+    t.rows = static_cast<int>(n - full * 256);
+    if (t.rows <= 128) {
+      t.n0 = item * 512;
+      return 1;
+    }
+    t.n0 = item * 256;
+    return 0;
+  }
+  return -1;
+}
+
+// Grouped GEMM with both tile shapes in one launch; the two 80 KB LDS halves hold one stage
+// each (activation rows first, then weight rows), which fits either shape.
+__global__ __launch_bounds__(kThreads, 1) void gemm_grouped_kernel(
+    const uint8_t *__restrict__ xq, const float *__restrict__ sa, const uint8_t *__restrict__ wq,
+    const float *__restrict__ sb, const int32_t *__restrict__ offsets, int G, int64_t M, int64_t N,
+    int64_t K, void *__restrict__ c, int out_f32) {
+  constexpr int kHalf = 80 * 1024;
+  __shared__ __attribute__((aligned(1024))) uint8_t sbuf0[kHalf];
+  __shared__ __attribute__((aligned(1024))) uint8_t sbuf1[kHalf];
+  FP8Q_LDS uint8_t *b0 = (FP8Q_LDS uint8_t *)sbuf0;
+  FP8Q_LDS uint8_t *b1 = (FP8Q_LDS uint8_t *)sbuf1;
+  Tile t;
+  const int shape = grouped_item(offsets, G, M, N, K, wq, sb, t);
+  if (shape < 0) return;
+  t.x = xq;
+  if (shape == 0) {
+    const Stages st = {b0, b0 + 256 * kBK, b1, b1 + 256 * kBK, nullptr, nullptr};
+    gemm_tile<8, false, 4>(t, sa, M, N, K, c, out_f32, st);
+  } else {
+    const Stages st = {b0, b0 + 128 * kBK, b1, b1 + 128 * kBK, nullptr, nullptr};
+    gemm_tile<8, false, 2>(t, sa, M, N, K, c, out_f32, st);
   }
 }
 
@@ -548,9 +608,8 @@ hipError_t launch_gemm(const uint8_t *xq, const float *sa, const uint8_t *wq, co
     }
   }
   if (best_a < 0) {
-    hipLaunchKernelGGL((gemm_blockscaled_kernel<8, false>), dim3(static_cast<uint32_t>(tiles)), dim3(kThreads), 0,
-                       stream, xq, sa, wq, sb, static_cast<const int32_t *>(nullptr), 1, M, N, K, c,
-                       out_f32 ? 1 : 0);
+    hipLaunchKernelGGL((gemm_blockscaled_kernel<8>), dim3(static_cast<uint32_t>(tiles)), dim3(kThreads), 0,
+                       stream, xq, sa, wq, sb, M, N, K, c, out_f32 ? 1 : 0);
   } else {
     const int64_t t1 = tm * best_a;
     const int64_t t2 = tm * ((N - best_a * 256 + 191) / 192);
@@ -580,10 +639,11 @@ hipError_t launch_grouped_gemm(const uint8_t *xq, const float *sa, const uint8_t
   // Upper bound on sum_g ceil(n_g / 256) without reading the offsets on the host.
   const int64_t slots = (M_tot + kBM - 1) / kBM + G;
   const int64_t tiles_n = (N + 255) / 256;
-  if (slots > 0x7fffffff || tiles_n > 65535 || G > 0x7fffffff) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<uint32_t>(slots), static_cast<uint32_t>(tiles_n));
-  hipLaunchKernelGGL((gemm_blockscaled_kernel<8, true>), grid, dim3(kThreads), 0, stream, xq, sa, wq, sb, offsets,
-                     static_cast<int>(G), M_tot, N, K, c, out_f32 ? 1 : 0);
+  if (slots * tiles_n > 0x7fffffff || G > 0x7fffffff) return hipErrorInvalidValue;
+  // Upper bound on the number of work items (sum over experts of ceil(n_g/256) rows of
+  // 256-wide tiles) without reading the offsets on the host; surplus workgroups exit.
+  hipLaunchKernelGGL(gemm_grouped_kernel, dim3(static_cast<uint32_t>(slots * tiles_n)), dim3(kThreads), 0, stream,
+                     xq, sa, wq, sb, offsets, static_cast<int>(G), M_tot, N, K, c, out_f32 ? 1 : 0);
   return hipGetLastError();
 }
 
