@@ -410,27 +410,36 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(
   gemm_tile<NFR>(t, sa, M, N, K, c, out_f32, st);
 }
 
-// Dense problem in two column ranges of different tile widths, one launch: workgroups
+// Dense problem in two column ranges of different tile widths, one launch: tiles
 // [0, tiles1) cover columns [0, n_split) with 32*NFR1-wide tiles, the rest cover
-// [n_split, N) with 32*NFR2-wide tiles.  Workgroups start in index order, so the wide
-// tiles take the first round and the narrow ones fill what would otherwise be a partly
-// idle last round.
+// [n_split, N) with 32*NFR2-wide tiles (tiles1 == total: one width throughout).  Tiles are
+// taken in index order, so the wide tiles take the first round and the narrow ones fill
+// what would otherwise be a partly idle last round.
+//
+// Persistent: the grid has at most one workgroup per CU and workgroup b takes tiles b,
+// b + gridDim.x, ... (a multiple of 8 keeps every tile on the XCD the mapping assigns it),
+// so a CU starts its next tile's copies while the previous tile's output stores drain,
+// instead of retiring the workgroup and launching a new one.
 template <int NFR1, int NFR2>
 __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_split_kernel(
     const uint8_t *__restrict__ xq, const float *__restrict__ sa, const uint8_t *__restrict__ wq,
-    const float *__restrict__ sb, int64_t M, int64_t N, int64_t K, int64_t n_split, int tiles1,
+    const float *__restrict__ sb, int64_t M, int64_t N, int64_t K, int64_t n_split, int tiles1, int total,
     void *__restrict__ c, int out_f32) {
   FP8Q_DECLARE_STAGES(st, 16);
-  Tile t;
-  const int bid = blockIdx.x;
-  if (bid < tiles1) {
-    dense_tile<32 * NFR1>(bid, M, 0, n_split, wq, sb, t);
-    t.x = xq;
-    gemm_tile<NFR1>(t, sa, M, N, K, c, out_f32, st);
-  } else {
-    dense_tile<32 * NFR2>(bid - tiles1, M, n_split, N, wq, sb, t);
-    t.x = xq;
-    gemm_tile<NFR2>(t, sa, M, N, K, c, out_f32, st);
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    Tile t;
+    if (item < tiles1) {
+      dense_tile<32 * NFR1>(item, M, 0, n_split, wq, sb, t);
+      t.x = xq;
+      gemm_tile<NFR1>(t, sa, M, N, K, c, out_f32, st);
+    } else {
+      dense_tile<32 * NFR2>(item - tiles1, M, n_split, N, wq, sb, t);
+      t.x = xq;
+      gemm_tile<NFR2>(t, sa, M, N, K, c, out_f32, st);
+    }
+    // Every wave is past its last LDS read (its data fed the MFMAs) before the next tile's
+    // first copy overwrites the stage buffers.  A bare barrier: no wait for the stores.
+    __builtin_amdgcn_s_barrier();
   }
 }
 
@@ -576,6 +585,9 @@ double makespan(int64_t n1, int64_t n2, double c2, int64_t cus) {
 #ifndef FP8Q_SPLIT
 #define FP8Q_SPLIT 1
 #endif
+#ifndef FP8Q_PERSISTENT
+#define FP8Q_PERSISTENT 1
+#endif
 
 hipError_t launch_gemm(const uint8_t *xq, const float *sa, const uint8_t *wq, const float *sb,
                        int64_t M, int64_t N, int64_t K, void *c, bool out_f32, hipStream_t stream) {
@@ -607,16 +619,16 @@ hipError_t launch_gemm(const uint8_t *xq, const float *sa, const uint8_t *wq, co
       }
     }
   }
-  if (best_a < 0) {
-    hipLaunchKernelGGL((gemm_blockscaled_kernel<8>), dim3(static_cast<uint32_t>(tiles)), dim3(kThreads), 0,
-                       stream, xq, sa, wq, sb, M, N, K, c, out_f32 ? 1 : 0);
-  } else {
-    const int64_t t1 = tm * best_a;
-    const int64_t t2 = tm * ((N - best_a * 256 + 191) / 192);
-    if (t1 + t2 > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_blockscaled_split_kernel<8, 6>), dim3(static_cast<uint32_t>(t1 + t2)), dim3(kThreads),
-                       0, stream, xq, sa, wq, sb, M, N, K, best_a * 256, static_cast<int>(t1), c, out_f32 ? 1 : 0);
-  }
+  // uniform 256-wide tiles are the split launch with every tile in the first range
+  const int64_t t1 = best_a < 0 ? tiles : tm * best_a;
+  const int64_t t2 = best_a < 0 ? 0 : tm * ((N - best_a * 256 + 191) / 192);
+  const int64_t n_split = best_a < 0 ? N : best_a * 256;
+  if (t1 + t2 > 0x7fffffff) return hipErrorInvalidValue;
+  const int64_t total = t1 + t2;
+  const int64_t grid = FP8Q_PERSISTENT ? min(total, (cus / 8) * 8 > 0 ? (cus / 8) * 8 : cus) : total;
+  hipLaunchKernelGGL((gemm_blockscaled_split_kernel<8, 6>), dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0,
+                     stream, xq, sa, wq, sb, M, N, K, n_split, static_cast<int>(t1), static_cast<int>(total), c,
+                     out_f32 ? 1 : 0);
   return hipGetLastError();
 }
 
