@@ -37,5 +37,6 @@ Modules:
     backward -- dgrad / wgrad of a linear layer: transposed weight blocks, 128x1
               token tiles, the GEMM with per-row scales on both operands
     swiglu -- SwiGLU of the expert up-projection output followed by the 1x128 quantizer
+    comparators -- tensor-level and delayed (historical-max) scaling, for the accuracy study
 """
-from . import e4m3, quant, gemm, backward, swiglu  # noqa: F401
+from . import e4m3, quant, gemm, backward, swiglu, comparators  # noqa: F401
