@@ -34,12 +34,12 @@ LIB_PATH = os.environ.get("FP8Q_LIBRARY") or os.path.join(HERE, "libfp8q.so")
 FP8Q_OK = 0
 FP8Q_OUT_BF16 = 0
 FP8Q_OUT_F32 = 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 EXPORTED = ("fp8q_quantize_act_1x128", "fp8q_quantize_w_128x128", "fp8q_gemm_blockscaled",
             "fp8q_grouped_gemm_blockscaled", "fp8q_quantize_w_128x128_t", "fp8q_quantize_act_dual",
-            "fp8q_gemm_rowscaled", "fp8q_swiglu_quantize_act_1x128", "fp8q_status_string",
-            "fp8q_abi_version")
+            "fp8q_gemm_rowscaled", "fp8q_swiglu_quantize_act_1x128", "fp8q_quantize_per_tensor",
+            "fp8q_status_string", "fp8q_abi_version")
 
 
 class Fp8qError(RuntimeError):
@@ -69,9 +69,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp8q_quantize_act_dual.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
     lib.fp8q_gemm_rowscaled.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i32, vp]
     lib.fp8q_swiglu_quantize_act_1x128.argtypes = [vp, i64, i64, vp, vp, vp]
+    lib.fp8q_quantize_per_tensor.argtypes = [vp, i64, vp, vp, vp, vp]
     for name in ("fp8q_quantize_act_1x128", "fp8q_quantize_w_128x128", "fp8q_gemm_blockscaled",
                  "fp8q_grouped_gemm_blockscaled", "fp8q_quantize_w_128x128_t", "fp8q_quantize_act_dual",
-                 "fp8q_gemm_rowscaled", "fp8q_swiglu_quantize_act_1x128"):
+                 "fp8q_gemm_rowscaled", "fp8q_swiglu_quantize_act_1x128", "fp8q_quantize_per_tensor"):
         getattr(lib, name).restype = i32
     lib.fp8q_status_string.argtypes = [i32]
     lib.fp8q_status_string.restype = ctypes.c_char_p
@@ -242,6 +243,26 @@ def fp8q_swiglu_quantize_act_1x128(gu: torch.Tensor, xq=None, sa=None, stream=No
     return xq, sa
 
 
+def fp8q_quantize_per_tensor(x: torch.Tensor, scale: torch.Tensor | None = None, q=None, stats=None, stream=None):
+    """One scale for all of x (bf16, any shape, numel % 8 == 0): tensor-level scaling when
+    `scale` is None, else delayed scaling with that device float32 scale.  Returns
+    (q uint8 like x, stats int32 [3]: amax bits, saturated count, scale bits)."""
+    _need(x, torch.bfloat16, "x")
+    if scale is not None:
+        _need(scale, torch.float32, "scale")
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if q is None else q
+    stats = torch.empty(3, dtype=torch.int32, device=x.device) if stats is None else stats
+    _check(load_library().fp8q_quantize_per_tensor(_ptr(x), x.numel(), _ptr(scale), _ptr(q), _ptr(stats),
+                                                   _stream(stream)), "fp8q_quantize_per_tensor")
+    return q, stats
+
+
+def tensor_stats(stats: torch.Tensor):
+    """(amax, saturated count, scale) of a stats tensor from fp8q_quantize_per_tensor."""
+    h = stats.cpu()
+    return (float(h[0:1].view(torch.float32)), int(h[1]), float(h[2:3].view(torch.float32)))
+
+
 quantize_act_1x128 = fp8q_quantize_act_1x128
 quantize_w_128x128 = fp8q_quantize_w_128x128
 gemm_blockscaled = fp8q_gemm_blockscaled
@@ -250,3 +271,4 @@ quantize_w_128x128_t = fp8q_quantize_w_128x128_t
 quantize_act_dual = fp8q_quantize_act_dual
 gemm_rowscaled = fp8q_gemm_rowscaled
 swiglu_quantize_act_1x128 = fp8q_swiglu_quantize_act_1x128
+quantize_per_tensor = fp8q_quantize_per_tensor

@@ -138,6 +138,17 @@ fp8q_status fp8q_swiglu_quantize_act_1x128(const uint16_t *gu_bf16, int64_t M, i
   return launched(fp8q::launch_swiglu_quant_act(gu_bf16, M, I, xq, sa, as_stream(stream)));
 }
 
+fp8q_status fp8q_quantize_per_tensor(const uint16_t *x_bf16, int64_t n, const float *scale_in, uint8_t *q,
+                                     uint32_t *stats, void *stream) {
+  if (n < 0 || n % 8 != 0 || n >= kMaxElems) return FP8Q_ERR_SHAPE;
+  if (!stats) return FP8Q_ERR_NULL;
+  if (n > 0 && (!x_bf16 || !q)) return FP8Q_ERR_NULL;
+  if (misaligned(x_bf16) || misaligned(q) || misaligned(stats, 4) || misaligned(scale_in, 4))
+    return FP8Q_ERR_ALIGN;
+  if (device_ok() != FP8Q_OK) return FP8Q_ERR_DEVICE;
+  return launched(fp8q::launch_quant_per_tensor(x_bf16, n, scale_in, q, stats, as_stream(stream)));
+}
+
 const char *fp8q_status_string(fp8q_status status) {
   switch (status) {
     case FP8Q_OK: return "ok";

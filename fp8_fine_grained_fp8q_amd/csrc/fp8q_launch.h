@@ -23,6 +23,11 @@ hipError_t launch_quant_act_dual(const uint16_t *x, int64_t M, int64_t K, uint8_
 hipError_t launch_swiglu_quant_act(const uint16_t *gu, int64_t M, int64_t I, uint8_t *xq, float *sa,
                                    hipStream_t stream);
 
+// One scale for n BF16 values (n % 8 == 0): from the tensor's amax (scale_in null) or the
+// caller's scale; stats[0..2] = amax bits, saturated count, scale bits.
+hipError_t launch_quant_per_tensor(const uint16_t *x, int64_t n, const float *scale_in, uint8_t *q,
+                                   uint32_t *stats, hipStream_t stream);
+
 hipError_t launch_gemm(const uint8_t *xq, const float *sa, const uint8_t *wq, const float *sb,
                        int64_t M, int64_t N, int64_t K, void *c, bool out_f32, hipStream_t stream);
 

@@ -423,4 +423,85 @@ hipError_t launch_swiglu_quant_act(const uint16_t *gu, int64_t M, int64_t I, uin
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------------
+// Tensor-level and delayed scaling (the prior art, for accuracy comparisons): one scale for
+// a whole tensor of n BF16 values.  stats[0] = amax (float bits; a non-negative float's bits
+// order like unsigned integers, so an unsigned atomic max works), stats[1] = saturated
+// count, stats[2] = the scale used.  Three launches for tensor-level scaling (clear, amax,
+// quantize with amax / 448), two for delayed scaling (clear, quantize with the caller's
+// scale while taking the amax for the history).  Grid-stride loops over 16-byte chunks.
+// ---------------------------------------------------------------------------------------
+__global__ void tensor_stats_clear_kernel(uint32_t *__restrict__ stats) {
+  if (threadIdx.x < 3) stats[threadIdx.x] = 0u;
+}
+
+// Largest |x| of the workgroup's values, one unsigned atomic max per workgroup.
+__device__ __forceinline__ void block_amax_atomic(float m, uint32_t *stats) {
+  __shared__ float wmax[4];
+  m = row16_max(m);
+  m = fmaxf(fmaxf(lane_f32(m, 0), lane_f32(m, 16)), fmaxf(lane_f32(m, 32), lane_f32(m, 48)));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    atomicMax(stats, __float_as_uint(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]))));
+}
+
+__global__ __launch_bounds__(256) void tensor_amax_kernel(const uint16_t *__restrict__ x, int64_t chunks,
+                                                          uint32_t *__restrict__ stats) {
+  float m = 0.0f;
+  for (int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; c < chunks;
+       c += static_cast<int64_t>(gridDim.x) * 256)
+    m = fmaxf(m, absmax8(load16_stream(x + c * 8)));
+  block_amax_atomic(m, stats);
+}
+
+// kDelayed: scale from *scale_in (and the amax of x is taken for the history); else from
+// the amax already in stats[0].
+template <bool kDelayed>
+__global__ __launch_bounds__(256) void tensor_quant_kernel(const uint16_t *__restrict__ x, int64_t chunks,
+                                                           const float *__restrict__ scale_in,
+                                                           uint8_t *__restrict__ q, uint32_t *__restrict__ stats) {
+  const float s = kDelayed ? *scale_in : __uint_as_float(stats[0]) / kE4M3Max;
+  const GroupDiv dv(s);
+  float m = 0.0f;
+  uint32_t sat = 0;
+  for (int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; c < chunks;
+       c += static_cast<int64_t>(gridDim.x) * 256) {
+    const uint4 v = load16_stream(x + c * 8);
+    float y[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                  bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+    if (kDelayed) m = fmaxf(m, absmax8(v));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      y[i] = dv.mode == 1 ? dv.fast(y[i]) : (dv.mode == 2 ? y[i] / dv.s : y[i]);
+      sat += fabsf(y[i]) > kE4M3Max ? 1u : 0u;
+    }
+    uint2 out;
+    out.x = pack4_e4m3(y[0], y[1], y[2], y[3]);
+    out.y = pack4_e4m3(y[4], y[5], y[6], y[7]);
+    *reinterpret_cast<uint2 *>(q + c * 8) = out;
+  }
+  if (sat) atomicAdd(stats + 1, sat);
+  if (blockIdx.x == 0 && threadIdx.x == 0) stats[2] = __float_as_uint(s);
+  if (kDelayed) block_amax_atomic(m, stats);
+}
+
+hipError_t launch_quant_per_tensor(const uint16_t *x, int64_t n, const float *scale_in, uint8_t *q,
+                                   uint32_t *stats, hipStream_t stream) {
+  const int64_t chunks = n / 8;
+  const int64_t blocks = (chunks + 255) / 256 < 4096 ? (chunks + 255) / 256 : 4096;
+  hipLaunchKernelGGL(tensor_stats_clear_kernel, dim3(1), dim3(64), 0, stream, stats);
+  if (chunks == 0) return hipGetLastError();
+  if (scale_in == nullptr) {
+    hipLaunchKernelGGL(tensor_amax_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, x, chunks,
+                       stats);
+    hipLaunchKernelGGL(tensor_quant_kernel<false>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, x,
+                       chunks, scale_in, q, stats);
+  } else {
+    hipLaunchKernelGGL(tensor_quant_kernel<true>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, x,
+                       chunks, scale_in, q, stats);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace fp8q

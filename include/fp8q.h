@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define FP8Q_ABI_VERSION 3
+#define FP8Q_ABI_VERSION 4
 
 typedef int32_t fp8q_status;
 
@@ -195,6 +195,28 @@ fp8q_status fp8q_gemm_rowscaled(const uint8_t *aq, const float *sa, const uint8_
  */
 fp8q_status fp8q_swiglu_quantize_act_1x128(const uint16_t *gu_bf16, int64_t M, int64_t I, uint8_t *xq,
                                            float *sa, void *stream);
+
+/*
+ * Tensor-level and delayed FP8 scaling, the prior art the fine-grained online scheme is
+ * contrasted with (risenshineclean.com page, section 3, first bullet: 1x128 / 128x128
+ * groups versus traditional tensor-level quantization; codingmall.com page, section "Dinh
+ * luong truc tuyen": no delayed quantization from historical maxima).  For accuracy
+ * comparisons only: one scale for a whole tensor.
+ *   x_bf16   : n BF16 values (any layout), n % 8 == 0
+ *   scale_in : NULL for tensor-level scaling (scale = RN32(amax / 448) of x itself), or a
+ *              DEVICE float holding the scale to use (delayed scaling: the caller forms it
+ *              from the amax history, e.g. RN32(max(history) / 448))
+ *   q        : n E4M3 codes (out), code = E4M3(RN32(x / scale)), saturating at +-448
+ *   stats    : DEVICE uint32[3] (out): [0] = bits of the FP32 amax of x (for the history),
+ *              [1] = number of values whose quotient exceeded 448 and saturated,
+ *              [2] = bits of the FP32 scale used
+ * The codes feed fp8q_gemm_blockscaled with every tile / block scale equal to the tensor's
+ * scale.  n == 0 only clears stats.  Errors: FP8Q_ERR_SHAPE (n < 0 or n % 8 != 0),
+ * FP8Q_ERR_NULL, FP8Q_ERR_ALIGN (x, q 16-byte; stats, scale_in 4-byte), FP8Q_ERR_DEVICE,
+ * FP8Q_ERR_LAUNCH.
+ */
+fp8q_status fp8q_quantize_per_tensor(const uint16_t *x_bf16, int64_t n, const float *scale_in, uint8_t *q,
+                                     uint32_t *stats, void *stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *fp8q_status_string(fp8q_status status);

@@ -135,6 +135,18 @@ def test_swiglu_quantizer_argument_checks(lib):
     assert f(None, 0, 128, None, None, None) == E["FP8Q_OK"]
 
 
+def test_per_tensor_quantizer_argument_checks(lib):
+    E = header_enums()
+    A = ALIGNED
+    f = lib.fp8q_quantize_per_tensor
+    assert f(A, 12, None, A, A, None) == E["FP8Q_ERR_SHAPE"]
+    assert f(A, -8, None, A, A, None) == E["FP8Q_ERR_SHAPE"]
+    assert f(A, 64, None, A, None, None) == E["FP8Q_ERR_NULL"]
+    assert f(None, 64, None, A, A, None) == E["FP8Q_ERR_NULL"]
+    assert f(A + 8, 64, None, A, A, None) == E["FP8Q_ERR_ALIGN"]
+    assert f(A, 64, A + 2, A, A, None) == E["FP8Q_ERR_ALIGN"]
+
+
 def test_valid_call_without_gpu_reports_device_error(lib):
     """On a host without a GPU a well-formed call must fail cleanly, not crash."""
     import torch
