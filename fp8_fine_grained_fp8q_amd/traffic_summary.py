@@ -35,13 +35,13 @@ def dispatches(path, counter):
 
 def gemm_and_copy(rows):
     """Mean counter of the GEMM dispatches and median of the calibration copies."""
-    gemm = [v for _, n, v in rows if "gemm_blockscaled" in n]
+    gemm = [v for _, n, v in rows if "fp8q::gemm_" in n]
     cal = [v for i, (_, n, v) in enumerate(rows)
-           if i > 0 and "copy" in n.lower() and "gemm_blockscaled" in rows[i - 1][1]]
+           if i > 0 and "copy" in n.lower() and "fp8q::gemm_" in rows[i - 1][1]]
     if not gemm or not cal:
         raise SystemExit("no GEMM dispatch or no calibration copy in the counter file")
     cal.sort()
-    name = next(n for _, n, _ in rows if "gemm_blockscaled" in n)
+    name = next(n for _, n, _ in rows if "fp8q::gemm_" in n)
     return name, sum(gemm) / len(gemm), cal[len(cal) // 2]
 
 
