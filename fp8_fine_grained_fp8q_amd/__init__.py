@@ -105,9 +105,11 @@ def _check(status: int, what: str):
         raise Fp8qError(status, what)
 
 
-def _need(t: torch.Tensor, dtype, name: str):
+def _need(t: torch.Tensor, dtype, name: str, shape=None):
     if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous {dtype} CUDA tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
 def fp8q_quantize_act_1x128(x: torch.Tensor, xq: torch.Tensor | None = None,
@@ -119,6 +121,8 @@ def fp8q_quantize_act_1x128(x: torch.Tensor, xq: torch.Tensor | None = None,
         xq = torch.empty((M, K), dtype=torch.uint8, device=x.device)
     if sa is None:
         sa = torch.empty((K // 128, M), dtype=torch.float32, device=x.device)
+    _need(xq, torch.uint8, "xq", (M, K))
+    _need(sa, torch.float32, "sa", (K // 128, M))
     _check(load_library().fp8q_quantize_act_1x128(_ptr(x), M, K, _ptr(xq), _ptr(sa), _stream(stream)),
            "fp8q_quantize_act_1x128")
     return xq, sa
@@ -132,9 +136,11 @@ def fp8q_quantize_w_128x128(w: torch.Tensor, wq: torch.Tensor | None = None,
     G, N, K = (1, *w.shape) if squeeze else w.shape
     if wq is None:
         wq = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    shape = (N // 128, K // 128) if squeeze else (G, N // 128, K // 128)
     if sb is None:
-        shape = (N // 128, K // 128) if squeeze else (G, N // 128, K // 128)
         sb = torch.empty(shape, dtype=torch.float32, device=w.device)
+    _need(wq, torch.uint8, "wq", w.shape)
+    _need(sb, torch.float32, "sb", shape)
     _check(load_library().fp8q_quantize_w_128x128(_ptr(w), G, N, K, _ptr(wq), _ptr(sb), _stream(stream)),
            "fp8q_quantize_w_128x128")
     return wq, sb
@@ -156,9 +162,17 @@ def fp8q_gemm_blockscaled(xq, sa, wq, sb, out_dtype=torch.bfloat16, out: torch.T
     _need(sa, torch.float32, "sa")
     _need(sb, torch.float32, "sb")
     M, K = xq.shape
-    N = wq.shape[-2]
+    if wq.dim() == 3 and wq.shape[0] == 1:
+        wq, sb = wq[0], sb.reshape(sb.shape[-2:])
+    if wq.dim() != 2:
+        raise ValueError("the dense GEMM takes one weight matrix wq [N, K]; use the grouped GEMM for experts")
+    N = wq.shape[0]
+    _need(wq, torch.uint8, "wq", (N, K))
+    _need(sa, torch.float32, "sa", (K // 128, M))
+    _need(sb, torch.float32, "sb", (N // 128, K // 128))
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=xq.device)
+    _need(out, out.dtype, "out", (M, N))
     _check(load_library().fp8q_gemm_blockscaled(_ptr(xq), _ptr(sa), _ptr(wq), _ptr(sb), M, N, K, _ptr(out),
                                                 _out_code(out.dtype), _stream(stream)),
            "fp8q_gemm_blockscaled")
@@ -175,8 +189,13 @@ def fp8q_grouped_gemm_blockscaled(xq, sa, wq, sb, offsets, out_dtype=torch.bfloa
     _need(offsets, torch.int32, "offsets")
     M, K = xq.shape
     G, N, _ = wq.shape
+    _need(wq, torch.uint8, "wq", (G, N, K))
+    _need(sa, torch.float32, "sa", (K // 128, M))
+    _need(sb, torch.float32, "sb", (G, N // 128, K // 128))
+    _need(offsets, torch.int32, "offsets", (G + 1,))
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=xq.device)
+    _need(out, out.dtype, "out", (M, N))
     _check(load_library().fp8q_grouped_gemm_blockscaled(
         _ptr(xq), _ptr(sa), _ptr(wq), _ptr(sb), _ptr(offsets), G, M, N, K, _ptr(out),
         _out_code(out.dtype), _stream(stream)), "fp8q_grouped_gemm_blockscaled")
@@ -195,6 +214,10 @@ def fp8q_quantize_w_128x128_t(w: torch.Tensor, wq=None, sb=None, wqt=None, sbt=N
     sb = torch.empty(lead + (N // 128, K // 128), dtype=torch.float32, device=dev) if sb is None else sb
     wqt = torch.empty(lead + (K, N), dtype=torch.uint8, device=dev) if wqt is None else wqt
     sbt = torch.empty(lead + (K // 128, N // 128), dtype=torch.float32, device=dev) if sbt is None else sbt
+    _need(wq, torch.uint8, "wq", w.shape)
+    _need(sb, torch.float32, "sb", lead + (N // 128, K // 128))
+    _need(wqt, torch.uint8, "wqt", lead + (K, N))
+    _need(sbt, torch.float32, "sbt", lead + (K // 128, N // 128))
     _check(load_library().fp8q_quantize_w_128x128_t(_ptr(w), G, N, K, _ptr(wq), _ptr(sb), _ptr(wqt), _ptr(sbt),
                                                     _stream(stream)), "fp8q_quantize_w_128x128_t")
     return wq, sb, wqt, sbt
@@ -210,6 +233,10 @@ def fp8q_quantize_act_dual(x: torch.Tensor, xq=None, sa=None, xqt=None, sat=None
     sa = torch.empty((K // 128, M), dtype=torch.float32, device=dev) if sa is None else sa
     xqt = torch.empty((K, M), dtype=torch.uint8, device=dev) if xqt is None else xqt
     sat = torch.empty((M // 128, K), dtype=torch.float32, device=dev) if sat is None else sat
+    _need(xq, torch.uint8, "xq", (M, K))
+    _need(sa, torch.float32, "sa", (K // 128, M))
+    _need(xqt, torch.uint8, "xqt", (K, M))
+    _need(sat, torch.float32, "sat", (M // 128, K))
     _check(load_library().fp8q_quantize_act_dual(_ptr(x), M, K, _ptr(xq), _ptr(sa), _ptr(xqt), _ptr(sat),
                                                  _stream(stream)), "fp8q_quantize_act_dual")
     return xq, sa, xqt, sat
@@ -224,8 +251,12 @@ def fp8q_gemm_rowscaled(aq, sa, bq, sb, out_dtype=torch.bfloat16, out: torch.Ten
     _need(sb, torch.float32, "sb")
     P, Kc = aq.shape
     Q = bq.shape[0]
+    _need(bq, torch.uint8, "bq", (Q, Kc))
+    _need(sa, torch.float32, "sa", (Kc // 128, P))
+    _need(sb, torch.float32, "sb", (Kc // 128, Q))
     if out is None:
         out = torch.empty((P, Q), dtype=out_dtype, device=aq.device)
+    _need(out, out.dtype, "out", (P, Q))
     _check(load_library().fp8q_gemm_rowscaled(_ptr(aq), _ptr(sa), _ptr(bq), _ptr(sb), P, Q, Kc, _ptr(out),
                                               _out_code(out.dtype), _stream(stream)), "fp8q_gemm_rowscaled")
     return out
@@ -238,6 +269,8 @@ def fp8q_swiglu_quantize_act_1x128(gu: torch.Tensor, xq=None, sa=None, stream=No
     I = I2 // 2
     xq = torch.empty((M, I), dtype=torch.uint8, device=gu.device) if xq is None else xq
     sa = torch.empty((I // 128, M), dtype=torch.float32, device=gu.device) if sa is None else sa
+    _need(xq, torch.uint8, "xq", (M, I))
+    _need(sa, torch.float32, "sa", (I // 128, M))
     _check(load_library().fp8q_swiglu_quantize_act_1x128(_ptr(gu), M, I, _ptr(xq), _ptr(sa), _stream(stream)),
            "fp8q_swiglu_quantize_act_1x128")
     return xq, sa
@@ -252,6 +285,10 @@ def fp8q_quantize_per_tensor(x: torch.Tensor, scale: torch.Tensor | None = None,
         _need(scale, torch.float32, "scale")
     q = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if q is None else q
     stats = torch.empty(3, dtype=torch.int32, device=x.device) if stats is None else stats
+    _need(q, torch.uint8, "q", x.shape)
+    _need(stats, torch.int32, "stats", (3,))
+    if scale is not None and scale.numel() != 1:
+        raise ValueError("scale must hold one float32")
     _check(load_library().fp8q_quantize_per_tensor(_ptr(x), x.numel(), _ptr(scale), _ptr(q), _ptr(stats),
                                                    _stream(stream)), "fp8q_quantize_per_tensor")
     return q, stats

@@ -10,6 +10,7 @@ namespace {
 
 constexpr int64_t kMaxDim = int64_t(1) << 31;
 constexpr int64_t kMaxElems = int64_t(1) << 62;
+constexpr int64_t kMaxGemmK = int64_t(1) << 22;
 
 bool misaligned(const void *p, uintptr_t a = 16) { return (reinterpret_cast<uintptr_t>(p) % a) != 0; }
 
@@ -32,6 +33,9 @@ fp8q_status check_gemm(const uint8_t *xq, const float *sa, const uint8_t *wq, co
   if (out_dtype != FP8Q_OUT_BF16 && out_dtype != FP8Q_OUT_F32) return FP8Q_ERR_DTYPE;
   if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return FP8Q_ERR_SHAPE;
   if (K < 128 || K % 128 != 0 || N % 128 != 0) return FP8Q_ERR_SHAPE;
+  // The kernels address a stage of up to 512 operand rows with 32-bit buffer offsets
+  // (row * K + byte), so K is limited to 2^22.
+  if (K > kMaxGemmK) return FP8Q_ERR_SHAPE;
   if (too_many(M, K) || too_many(N, K) || too_many(M, N)) return FP8Q_ERR_SHAPE;
   if (M == 0 || N == 0) return 1;  // nothing to do (positive: caller returns FP8Q_OK)
   if (!xq || !sa || !wq || !sb || !c) return FP8Q_ERR_NULL;

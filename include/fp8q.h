@@ -37,7 +37,9 @@
  *    Calls are asynchronous on it and never synchronize the host.
  *  - Arguments are checked before any HIP call; a failed check returns a negative
  *    fp8q_status and launches nothing.  M == 0 (or M_tot == 0) is a no-op FP8Q_OK.
- *  - Base pointers must be 16-byte aligned.  K and N must be multiples of 128.
+ *  - Base pointers must be 16-byte aligned.  K and N must be multiples of 128.  The GEMMs
+ *    take K (the contraction length) up to 4 194 304 (2^22): their kernels address the
+ *    operand stages with 32-bit offsets; larger K returns FP8Q_ERR_SHAPE.
  *  - The library allocates no device memory and keeps no mutable global state:
  *    calls are reentrant and thread-safe.  Kernel faults surface at the caller's
  *    next synchronization of `stream`.

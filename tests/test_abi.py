@@ -89,6 +89,8 @@ def test_gemm_argument_checks(lib):
     assert g(A, A, A, A, 4, 128, 128, None, 0, None) == E["FP8Q_ERR_NULL"]
     assert g(A, A, A + 1, A, 4, 128, 128, A, 0, None) == E["FP8Q_ERR_ALIGN"]
     assert g(None, None, None, None, 0, 128, 128, None, 0, None) == E["FP8Q_OK"]
+    assert g(A, A, A, A, 4, 128, (1 << 22) + 128, A, 0, None) == E["FP8Q_ERR_SHAPE"]   # 32-bit stage offsets
+    assert lib.fp8q_gemm_rowscaled(A, A, A, A, 4, 128, (1 << 22) + 128, A, 0, None) == E["FP8Q_ERR_SHAPE"]
     gg = lib.fp8q_grouped_gemm_blockscaled
     assert gg(A, A, A, A, A, 0, 4, 128, 128, A, 0, None) == E["FP8Q_ERR_SHAPE"]
     assert gg(A, A, A, A, None, 2, 4, 128, 128, A, 0, None) == E["FP8Q_ERR_NULL"]

@@ -270,3 +270,20 @@ def test_moe_workloads_sampled(name):
         wh = oq.dequant_w(wq_g, sb_g)
         assert_gemm_within_tol(got[lo:hi], xh @ wh.T, np.linalg.norm(xh, axis=1),
                                np.linalg.norm(wh, axis=1), f"{name} expert {g}")
+
+
+def test_binding_rejects_inconsistent_shapes():
+    """The binding checks every buffer's shape against the sizes it passes to the C ABI
+    (plain pointers there), so a mismatched scale or output tensor never reaches a kernel."""
+    xq, sa, wq, sb = (dev(a) for a in quantized(64, 256, 256, seed=1))
+    with pytest.raises(ValueError):
+        fq.fp8q_gemm_blockscaled(xq, sa[:1], wq, sb)
+    with pytest.raises(ValueError):
+        fq.fp8q_gemm_blockscaled(xq, sa, wq, sb[:1])
+    with pytest.raises(ValueError):
+        fq.fp8q_gemm_blockscaled(xq, sa, wq, sb, out=torch.empty((64, 128), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError):
+        fq.fp8q_quantize_act_1x128(torch.zeros((64, 256), dtype=torch.bfloat16, device="cuda"),
+                                   sa=torch.empty((1, 64), device="cuda"))
+    with pytest.raises(ValueError):
+        fq.fp8q_grouped_gemm_blockscaled(xq, sa, wq[None], sb[None], torch.zeros(3, dtype=torch.int32, device="cuda"))
