@@ -50,15 +50,10 @@ constexpr int kGroupM = 8;  // M tiles per raster group (L2 reuse of weight pane
 #ifndef FP8Q_PRIO
 #define FP8Q_PRIO 1
 #endif
-#ifndef FP8Q_SWZ_MODE
-#define FP8Q_SWZ_MODE 1
-#endif
-// XOR swizzle of the 16-byte chunk index by row.  Mode 1 spreads rows 2i and 2i+1 over
-// the two 128-byte halves of a 256-byte bank line and pairs i over the 8 chunk slots
-// (conflict-free for 16 lanes with 64 banks of 4 bytes); mode 0 separates 8 rows.
-__device__ __forceinline__ int swz(int row) {
-  return FP8Q_SWZ_MODE == 2 ? 0 : FP8Q_SWZ_MODE ? ((row >> 1) & 7) : (row & 7);
-}
+// XOR swizzle of the 16-byte chunk index by row: rows 2i and 2i+1 go to the two 128-byte
+// halves of a 256-byte bank line and pairs i spread over the 8 chunk slots, so the 16 rows
+// of a fragment read (ds_read_b128) hit distinct banks.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 // Buffer resource (gfx9 family layout) over `bytes` bytes at `p`; loads at or past the
 // end return zeros, which is how rows beyond the tile's valid range are filled.
@@ -83,7 +78,7 @@ __device__ __forceinline__ void stage_offsets(int64_t K, int wave, int lane, uin
 }
 
 // Copy one stage (K bytes [koff, koff + 128) of 64*NL operand rows) into LDS.  Rows past
-// the resource's end (a 224-row weight tile, a ragged edge) are filled with zeros by the
+// the resource's end (a narrower weight tile, a ragged edge) are filled with zeros by the
 // buffer bounds check without touching memory, so every wave always issues NL loads and
 // the loop body stays free of branches.
 template <int NL = 4>
@@ -397,18 +392,6 @@ __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict
   const Stages st = {(FP8Q_LDS uint8_t *)sx0, (FP8Q_LDS uint8_t *)sw0,   \
                      (FP8Q_LDS uint8_t *)sx1, (FP8Q_LDS uint8_t *)sw1,   \
                      (FP8Q_LDS uint8_t *)sc0, (FP8Q_LDS uint8_t *)sc1}
-
-// Dense problem, one tile width throughout (1-D grid).
-template <int NFR>
-__global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_kernel(
-    const uint8_t *__restrict__ xq, const float *__restrict__ sa, const uint8_t *__restrict__ wq,
-    const float *__restrict__ sb, int64_t M, int64_t N, int64_t K, void *__restrict__ c, int out_f32) {
-  FP8Q_DECLARE_STAGES(st, 16);
-  Tile t;
-  dense_tile<32 * NFR>(blockIdx.x, M, 0, N, wq, sb, t);
-  t.x = xq;
-  gemm_tile<NFR>(t, sa, M, N, K, c, out_f32, st);
-}
 
 // Dense problem in two column ranges of different tile widths, one launch: tiles
 // [0, tiles1) cover columns [0, n_split) with 32*NFR1-wide tiles, the rest cover
