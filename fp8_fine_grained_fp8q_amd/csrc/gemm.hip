@@ -349,8 +349,9 @@ __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict
 #pragma unroll
   for (int f = 0; f < 4; ++f)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      acc[f][NFR - 1][i] = __builtin_fmaf(pp[f][i], kRowB ? sa_prev[f] * sbc_prev[i] : sclp[f], acc[f][NFR - 1][i]);
+    for (int i = 0; i < 4; ++i)  // the same operation order as the folds inside the loop
+      acc[f][NFR - 1][i] = kRowB ? __builtin_fmaf(pp[f][i] * sbc_prev[i], sa_prev[f], acc[f][NFR - 1][i])
+                                 : __builtin_fmaf(pp[f][i], sclp[f], acc[f][NFR - 1][i]);
 
   // Epilogue: lane owns row m = m_begin + wm*64 + f*16 + l16 and columns
   // n0 + wn*kWN + j*16 + 4*kg + {0..3}.
@@ -403,22 +404,25 @@ __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict
 // b + gridDim.x, ... (a multiple of 8 keeps every tile on the XCD the mapping assigns it),
 // so a CU starts its next tile's copies while the previous tile's output stores drain,
 // instead of retiring the workgroup and launching a new one.
-template <int NFR1, int NFR2>
+//
+// kRowB: the B operand carries 1x128 row-tile scales sb[K/128][N] (the weight-gradient GEMM
+// over token tiles) instead of 128x128 block scales.
+template <int NFR1, int NFR2, bool kRowB = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_split_kernel(
     const uint8_t *__restrict__ xq, const float *__restrict__ sa, const uint8_t *__restrict__ wq,
     const float *__restrict__ sb, int64_t M, int64_t N, int64_t K, int64_t n_split, int tiles1, int total,
     void *__restrict__ c, int out_f32) {
-  FP8Q_DECLARE_STAGES(st, 16);
+  FP8Q_DECLARE_STAGES(st, kRowB ? 1024 : 16);
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     Tile t;
     if (item < tiles1) {
       dense_tile<32 * NFR1>(item, M, 0, n_split, wq, sb, t);
       t.x = xq;
-      gemm_tile<NFR1>(t, sa, M, N, K, c, out_f32, st);
+      gemm_tile<NFR1, kRowB>(t, sa, M, N, K, c, out_f32, st);
     } else {
       dense_tile<32 * NFR2>(item - tiles1, M, n_split, N, wq, sb, t);
       t.x = xq;
-      gemm_tile<NFR2>(t, sa, M, N, K, c, out_f32, st);
+      gemm_tile<NFR2, kRowB>(t, sa, M, N, K, c, out_f32, st);
     }
     // Every wave is past its last LDS read (its data fed the MFMAs) before the next tile's
     // first copy overwrites the stage buffers.  A bare barrier: no wait for the stores.
@@ -515,19 +519,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_grouped_kernel(
   }
 }
 
-// Both operands with per-row 1x128 scales (the weight-gradient GEMM dW = dY^T X over
-// token tiles): A = xq with sa[K/128][M], B = wq[N][K] with sb[K/128][N]; uniform tiles.
-template <int NFR>
-__global__ __launch_bounds__(kThreads, 1) void gemm_rowscaled_kernel(
-    const uint8_t *__restrict__ xq, const float *__restrict__ sa, const uint8_t *__restrict__ wq,
-    const float *__restrict__ sb, int64_t M, int64_t N, int64_t K, void *__restrict__ c, int out_f32) {
-  FP8Q_DECLARE_STAGES(st, 1024);
-  Tile t;
-  dense_tile<32 * NFR>(blockIdx.x, M, 0, N, wq, sb, t);
-  t.x = xq;
-  gemm_tile<NFR, true>(t, sa, M, N, K, c, out_f32, st);
-}
-
 namespace {
 
 int device_cus() {
@@ -572,19 +563,22 @@ double makespan(int64_t n1, int64_t n2, double c2, int64_t cus) {
 #define FP8Q_PERSISTENT 1
 #endif
 
-hipError_t launch_gemm(const uint8_t *xq, const float *sa, const uint8_t *wq, const float *sb,
-                       int64_t M, int64_t N, int64_t K, void *c, bool out_f32, hipStream_t stream) {
-  const int64_t cus = device_cus();
+namespace {
+
+// Tile plan of a dense problem: uniform 256-wide tiles (t2 == 0, n_split == N), or the
+// first a*256 columns in 256-wide tiles and the rest in 192-wide ones, whichever finishes
+// first by the cost model (a 192-wide tile costs FP8Q_NARROW_COST of a 256-wide one).
+// FP8Q_DENSE_SPLIT overrides the choice (for tests): "off" = uniform, an integer a >= 0 =
+// split after a*256 columns (clamped below N).
+struct Plan {
+  int64_t t1, t2, n_split;
+};
+
+Plan dense_plan(int64_t M, int64_t N, int64_t cus) {
   const int64_t tm = (M + kBM - 1) / kBM;
   const int64_t tiles = tm * ((N + 255) / 256);
-  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  // Uniform 256-wide tiles, or the first a*256 columns in 256-wide tiles and the rest in
-  // 192-wide ones, whichever finishes first by the cost model (a 192-wide tile costs
-  // FP8Q_NARROW_COST of a 256-wide one: fewer MFMAs, nearly the same copies per step).
   double best = makespan(tiles, 0, 0.0, cus);
   int64_t best_a = -1;
-  // FP8Q_DENSE_SPLIT overrides the choice (for tests): "off" = uniform 256-wide tiles, an
-  // integer a >= 0 = split after a*256 columns (clamped below N).
   const char *force = getenv("FP8Q_DENSE_SPLIT");
   if (force && force[0] && strcmp(force, "auto") != 0) {
     if (strcmp(force, "off") != 0) {
@@ -602,30 +596,35 @@ hipError_t launch_gemm(const uint8_t *xq, const float *sa, const uint8_t *wq, co
       }
     }
   }
-  // uniform 256-wide tiles are the split launch with every tile in the first range
-  const int64_t t1 = best_a < 0 ? tiles : tm * best_a;
-  const int64_t t2 = best_a < 0 ? 0 : tm * ((N - best_a * 256 + 191) / 192);
-  const int64_t n_split = best_a < 0 ? N : best_a * 256;
-  if (t1 + t2 > 0x7fffffff) return hipErrorInvalidValue;
-  const int64_t total = t1 + t2;
+  if (best_a < 0) return {tiles, 0, N};
+  return {tm * best_a, tm * ((N - best_a * 256 + 191) / 192), best_a * 256};
+}
+
+template <bool kRowB>
+hipError_t launch_dense(const uint8_t *xq, const float *sa, const uint8_t *wq, const float *sb, int64_t M,
+                        int64_t N, int64_t K, void *c, bool out_f32, hipStream_t stream) {
+  const int64_t cus = device_cus();
+  const int64_t tm = (M + kBM - 1) / kBM;
+  if (tm * ((N + 191) / 192) > 0x7fffffff) return hipErrorInvalidValue;
+  const Plan p = dense_plan(M, N, cus);
+  const int64_t total = p.t1 + p.t2;
   const int64_t grid = FP8Q_PERSISTENT ? min(total, (cus / 8) * 8 > 0 ? (cus / 8) * 8 : cus) : total;
-  hipLaunchKernelGGL((gemm_blockscaled_split_kernel<8, 6>), dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0,
-                     stream, xq, sa, wq, sb, M, N, K, n_split, static_cast<int>(t1), static_cast<int>(total), c,
-                     out_f32 ? 1 : 0);
+  hipLaunchKernelGGL((gemm_blockscaled_split_kernel<8, 6, kRowB>), dim3(static_cast<uint32_t>(grid)),
+                     dim3(kThreads), 0, stream, xq, sa, wq, sb, M, N, K, p.n_split, static_cast<int>(p.t1),
+                     static_cast<int>(total), c, out_f32 ? 1 : 0);
   return hipGetLastError();
 }
 
-#ifndef FP8Q_ROWSCALED_NFR
-#define FP8Q_ROWSCALED_NFR 8
-#endif
+}  // namespace
+
+hipError_t launch_gemm(const uint8_t *xq, const float *sa, const uint8_t *wq, const float *sb,
+                       int64_t M, int64_t N, int64_t K, void *c, bool out_f32, hipStream_t stream) {
+  return launch_dense<false>(xq, sa, wq, sb, M, N, K, c, out_f32, stream);
+}
+
 hipError_t launch_gemm_rowscaled(const uint8_t *aq, const float *sa, const uint8_t *bq, const float *sb,
                                  int64_t M, int64_t N, int64_t K, void *c, bool out_f32, hipStream_t stream) {
-  constexpr int NFR = FP8Q_ROWSCALED_NFR;
-  const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + 32 * NFR - 1) / (32 * NFR));
-  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_rowscaled_kernel<NFR>), dim3(static_cast<uint32_t>(tiles)), dim3(kThreads), 0, stream,
-                     aq, sa, bq, sb, M, N, K, c, out_f32 ? 1 : 0);
-  return hipGetLastError();
+  return launch_dense<true>(aq, sa, bq, sb, M, N, K, c, out_f32, stream);
 }
 
 hipError_t launch_grouped_gemm(const uint8_t *xq, const float *sa, const uint8_t *wq, const float *sb,

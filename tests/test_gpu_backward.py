@@ -174,3 +174,23 @@ def test_wgrad_full_size_sampled():
     err = np.abs(g - ref)
     print(f"\n[wgrad 7168x7168 over 4096 tokens] max |err|/tol = {np.max(err / tol):.4f}")
     assert np.all(err <= tol)
+
+
+@pytest.mark.parametrize("P,Q,Kc", [(300, 1152, 512), (257, 640, 384)])
+def test_gemm_rowscaled_tile_plans(P, Q, Kc, monkeypatch):
+    """The row-scaled GEMM uses the dense tile plans too (uniform 256-wide tiles or a
+    256/192-wide column split); every plan meets the bar and all are bit-identical."""
+    rng = np.random.default_rng(P * 3 + Q + Kc)
+    aq, sa = oq.quantize_act_1x128(bf16(rng.standard_normal((P, Kc))))
+    bq, sb = oq.quantize_act_1x128(bf16(rng.standard_normal((Q, Kc)) * 2.0))
+    ref = ob.gemm_rowscaled(aq, sa, bq, sb)
+    outs = {}
+    for plan in ["off", "0", "1", "2", "auto"]:
+        monkeypatch.setenv("FP8Q_DENSE_SPLIT", plan)
+        got = fq.fp8q_gemm_rowscaled(dev(aq), dev(sa), dev(bq), dev(sb), out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        outs[plan] = host(got)
+        assert_gemm_within_tol(outs[plan], ref, ob.row_norms_rowscaled(aq, sa), ob.row_norms_rowscaled(bq, sb),
+                               f"rowscaled {P}x{Q}x{Kc} plan {plan}")
+    for plan in outs:
+        assert np.array_equal(outs[plan], outs["off"]), plan
