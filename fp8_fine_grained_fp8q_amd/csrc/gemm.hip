@@ -438,59 +438,88 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_split_kernel(
 // M tile last (tiles of one expert sharing a weight panel are adjacent), and workgroups are
 // dealt to the 8 XCDs in contiguous runs of items.  Returns the tile shape (0: 256 x 256,
 // 1: 128 x 512) or -1 past the last item.
+// A value the caller knows to be equal in every lane, moved to a scalar register (so tile
+// coordinates derived from lane shuffles still address the operands through SGPRs).
+__device__ __forceinline__ int uniform32(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(v, d);
+    v += lane >= d ? u : 0;
+  }
+  return v;
+}
+
 __device__ __forceinline__ int grouped_item(const int32_t *__restrict__ offsets, int G, int64_t M_tot, int64_t N,
                                             int64_t K, const uint8_t *wq, const float *sb, Tile &t) {
   const int nt_a = static_cast<int>((N + 255) / 256);
   const int nt_b = static_cast<int>((N + 511) / 512);
-  auto range = [&](int g, int64_t &a, int64_t &b) {
+  const int lane = threadIdx.x & 63;
+  // Expert g's clamped row range [a, b) and its number of work items (lanes past G: 0).
+  auto expert = [&](int g, int64_t &a, int64_t &b) -> int {
+    a = 0;
+    b = 0;
+    if (g >= G) return 0;
     a = offsets[g];
     b = offsets[g + 1];
     a = a < 0 ? 0 : (a > M_tot ? M_tot : a);
     b = b < a ? a : (b > M_tot ? M_tot : b);
+    const int64_t n = b - a, full = n / 256, tail = n % 256;
+    return static_cast<int>(full * nt_a + (tail == 0 ? 0 : (tail <= 128 ? nt_b : nt_a)));
   };
-  auto items_of = [&](int64_t n) {
-    const int64_t full = n / 256, tail = n % 256;
-    return full * nt_a + (tail == 0 ? 0 : (tail <= 128 ? nt_b : nt_a));
-  };
-  int64_t total = 0;
-  for (int g = 0; g < G; ++g) {
+  // The experts are scanned 64 at a time, one per lane (the grid bound keeps every count
+  // and the total below 2^31).
+  int total = 0;
+  for (int g0 = 0; g0 < G; g0 += 64) {
     int64_t a, b;
-    range(g, a, b);
-    total += items_of(b - a);
+    total += __shfl(wave_inclusive_sum(expert(g0 + lane, a, b)), 63);
   }
-  const int64_t bid = blockIdx.x;
+  total = uniform32(total);
+  const int bid = blockIdx.x;
   if (bid >= total) return -1;
-  const int64_t per = total / 8, rem = total % 8;
-  const int64_t xcd = bid % 8, idx = bid / 8;
-  int64_t item = xcd * per + (xcd < rem ? xcd : rem) + idx;
-  for (int g = 0; g < G; ++g) {
+  const int per = total / 8, rem = total % 8;
+  const int xcd = bid % 8, idx = bid / 8;
+  const int item = xcd * per + (xcd < rem ? xcd : rem) + idx;
+  int before = 0;
+  for (int g0 = 0; g0 < G; g0 += 64) {
     int64_t a, b;
-    range(g, a, b);
-    const int64_t n = b - a, cnt = items_of(n);
-    if (item >= cnt) {
-      item -= cnt;
-      continue;
-    }
-    t.w = wq + static_cast<int64_t>(g) * N * K;
-    t.sb = sb + static_cast<int64_t>(g) * (N / 128) * (K / 128);
-    t.n_end = N;
-    const int64_t full = n / 256;
-    if (item < full * nt_a) {
-      const int64_t nt = item / full, mt = item % full;
-      t.m_begin = a + mt * 256;
-      t.rows = 256;
-      t.n0 = nt * 256;
+    const int cnt = expert(g0 + lane, a, b);
+    const int incl = wave_inclusive_sum(cnt);
+    const int chunk = uniform32(__shfl(incl, 63));
+    if (item < before + chunk) {  // wave-uniform: the expert is in this chunk
+      const int gl = uniform32(__ffsll(static_cast<unsigned long long>(__ballot(before + incl > item))) - 1);
+      const int g = g0 + gl;
+      const int64_t ga = uniform64(__shfl(a, gl)), gb = uniform64(__shfl(b, gl));
+      int64_t it = uniform64(item - before - (__shfl(incl, gl) - __shfl(cnt, gl)));
+      t.w = wq + static_cast<int64_t>(g) * N * K;
+      t.sb = sb + static_cast<int64_t>(g) * (N / 128) * (K / 128);
+      t.n_end = N;
+      const int64_t n = gb - ga, full = n / 256;
+      if (it < full * nt_a) {
+        t.m_begin = ga + (it % full) * 256;
+        t.rows = 256;
+        t.n0 = (it / full) * 256;
+        return 0;
+      }
+      it -= full * nt_a;
+      t.m_begin = ga + full * 256;
+      t.rows = static_cast<int>(n - full * 256);
+      if (t.rows <= 128) {
+        t.n0 = it * 512;
+        return 1;
+      }
+      t.n0 = it * 256;
       return 0;
     }
-    item -= full * nt_a;
-    t.m_begin = a + full * 256;
-    t.rows = static_cast<int>(n - full * 256);
-    if (t.rows <= 128) {
-      t.n0 = item * 512;
-      return 1;
-    }
-    t.n0 = item * 256;
-    return 0;
+    before += chunk;
   }
   return -1;
 }

@@ -263,12 +263,21 @@ __global__ __launch_bounds__(256) void quant_act_dual_kernel(const uint16_t *__r
   uint4 v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = load16_stream(x + base + (r0 + 16 * i) * K);
+  // every value widened to FP32 once, shared by both orientations
+  float xv[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xv[i][e] = bf16_elem(v[i], e);
 
   // Row tiles (1x128 along K): the forward codes.
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float s = row16_max(absmax8(v[i])) / kE4M3Max;
-    *reinterpret_cast<uint2 *>(xq + base + (r0 + 16 * i) * K) = quant8(v[i], GroupDiv(s));
+    float m = fabsf(xv[i][0]);
+#pragma unroll
+    for (int e = 1; e < 8; ++e) m = fmaxf(m, fabsf(xv[i][e]));
+    const float s = row16_max(m) / kE4M3Max;
+    *reinterpret_cast<uint2 *>(xq + base + (r0 + 16 * i) * K) = quant8f(xv[i], GroupDiv(s));
     if (sub == 0) sa[kb * M + mb * 128 + r0 + 16 * i] = s;
   }
 
@@ -276,9 +285,9 @@ __global__ __launch_bounds__(256) void quant_act_dual_kernel(const uint16_t *__r
   float cm[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    float m = fabsf(bf16_elem(v[0], e));
+    float m = fabsf(xv[0][e]);
 #pragma unroll
-    for (int i = 1; i < 8; ++i) m = fmaxf(m, fabsf(bf16_elem(v[i], e)));
+    for (int i = 1; i < 8; ++i) m = fmaxf(m, fabsf(xv[i][e]));
     m = fmaxf(m, __shfl_xor(m, 16));
     m = fmaxf(m, __shfl_xor(m, 32));
     cm[e] = m;
@@ -313,14 +322,13 @@ __global__ __launch_bounds__(256) void quant_act_dual_kernel(const uint16_t *__r
     float y[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float xv = bf16_elem(v[i], e);
       if (all_fast) {
         GroupDiv d(0.0f);
         d.s = cs[e];
         d.r = cr[e];
-        y[e] = d.fast(xv);
+        y[e] = d.fast(xv[i][e]);
       } else {
-        y[e] = div_any(xv, cs[e], cr[e], cmode[e]);
+        y[e] = div_any(xv[i][e], cs[e], cr[e], cmode[e]);
       }
     }
     uint2 q;
