@@ -40,9 +40,13 @@
  *  - Base pointers must be 16-byte aligned.  K and N must be multiples of 128.  The GEMMs
  *    take K (the contraction length) up to 4 194 304 (2^22): their kernels address the
  *    operand stages with 32-bit offsets; larger K returns FP8Q_ERR_SHAPE.
- *  - The library allocates no device memory and keeps no mutable global state:
- *    calls are reentrant and thread-safe.  Kernel faults surface at the caller's
- *    next synchronization of `stream`.
+ *  - The library allocates no device memory; its only global state is a per-device
+ *    cache of the CU count (written once, the same value by any thread): calls are
+ *    reentrant and thread-safe.  Kernel faults surface at the caller's next
+ *    synchronization of `stream`.
+ *  - The dense GEMMs pick their tile plan from the shape and the CU count; the
+ *    environment variable FP8Q_DENSE_SPLIT ("off", or a count a of 256-wide tile
+ *    columns) overrides it for testing.  Every plan gives bit-identical results.
  */
 #ifndef FP8Q_H
 #define FP8Q_H
