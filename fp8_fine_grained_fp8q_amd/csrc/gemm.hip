@@ -662,7 +662,7 @@ hipError_t launch_grouped_gemm(const uint8_t *xq, const float *sa, const uint8_t
   // Upper bound on sum_g ceil(n_g / 256) without reading the offsets on the host.
   const int64_t slots = (M_tot + kBM - 1) / kBM + G;
   const int64_t tiles_n = (N + 255) / 256;
-  if (slots * tiles_n > 0x7fffffff || G > 0x7fffffff) return hipErrorInvalidValue;
+  if (slots * tiles_n > 0x7fffffff - 4096 || G > 0x7fffffff) return hipErrorInvalidValue;  // item indices stay in int
   // Upper bound on the number of work items (sum over experts of ceil(n_g/256) rows of
   // 256-wide tiles) without reading the offsets on the host; surplus workgroups exit.
   hipLaunchKernelGGL(gemm_grouped_kernel, dim3(static_cast<uint32_t>(slots * tiles_n)), dim3(kThreads), 0, stream,
