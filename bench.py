@@ -302,7 +302,7 @@ def run_train(args, torch, fq, dev):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library is a single-GPU implementation "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import torch
