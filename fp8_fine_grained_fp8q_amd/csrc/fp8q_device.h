@@ -78,6 +78,22 @@ struct GroupDiv {
     const float e2 = __builtin_fmaf(-y1, s, x);
     return __builtin_copysignf(__builtin_fmaf(e2, r, y1), x);
   }
+  // The same quotient for a dividend with at most 8 significant bits (every BF16 value),
+  // mode 1 only: q0 = RN(x*r) and a single correction, y = RN(q0 - e*r) with the residual
+  // taken negated, e = RN(q0*s - x).  One correction suffices for such dividends: checked
+  // exhaustively for all 128 BF16 significands against all 2^23 FP32 significands of s,
+  // every result equal to RN(x/s); the whole computation scales exactly with the exponents
+  // of x and s while no intermediate leaves the normal range, which the mode-1 bounds on s
+  // ensure for every quotient of magnitude >= 2^-11 (smaller ones are E4M3 zeros).  The
+  // negated residual keeps the sign of a zero dividend: x = -0 gives q0 = -0, e = +0 and
+  // y = -0 + -0 = -0.  The quotient must be finite: |x/s| stays far below the FP32 range
+  // whenever s is at least the group's amax / 448.
+  __device__ __forceinline__ float fast_bf16(float x) const {
+#pragma clang fp contract(off)
+    const float q0 = x * r;
+    const float en = __builtin_fmaf(q0, s, -x);
+    return __builtin_fmaf(-en, r, q0);
+  }
 };
 
 // Saturate to the E4M3 range (keeps -0), then pack four FP32 values into four E4M3 bytes
@@ -97,7 +113,7 @@ __device__ __forceinline__ uint2 quant8(const uint4 v, const GroupDiv &dv) {
                 bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
   if (dv.mode == 1) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = dv.fast(y[i]);
+    for (int i = 0; i < 8; ++i) y[i] = dv.fast_bf16(y[i]);
   } else if (dv.mode == 2) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = y[i] / dv.s;
@@ -108,15 +124,17 @@ __device__ __forceinline__ uint2 quant8(const uint4 v, const GroupDiv &dv) {
   return out;
 }
 
-// Eight FP32 values -> eight E4M3 codes with divisor `dv` (as quant8, for values that are
-// not BF16 inputs, e.g. a fused producer's FP32 output).
+// Eight FP32 values -> eight E4M3 codes with divisor `dv` (as quant8, for values held as
+// FP32: kBf16Values when each is a widened BF16 value, else any FP32 value, e.g. a fused
+// producer's output, which takes the two-correction division).
+template <bool kBf16Values>
 __device__ __forceinline__ uint2 quant8f(const float (&x)[8], const GroupDiv &dv) {
   float y[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) y[i] = x[i];
   if (dv.mode == 1) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = dv.fast(y[i]);
+    for (int i = 0; i < 8; ++i) y[i] = kBf16Values ? dv.fast_bf16(y[i]) : dv.fast(y[i]);
   } else if (dv.mode == 2) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = y[i] / dv.s;

@@ -225,13 +225,14 @@ hipError_t launch_quant_w(const uint16_t *w, int64_t G, int64_t N, int64_t K, ui
 // The token count M must be a multiple of 128.
 // ---------------------------------------------------------------------------------------
 
-// y = RN32(x / s) for a divisor held as (s, r, mode) in the GroupDiv convention.
+// y = RN32(x / s) of a BF16 value x for a divisor held as (s, r, mode) in the GroupDiv
+// convention.
 __device__ __forceinline__ float div_any(float x, float s, float r, int mode) {
   if (mode == 1) {
     GroupDiv d(0.0f);
     d.s = s;
     d.r = r;
-    return d.fast(x);
+    return d.fast_bf16(x);
   }
   return mode == 2 ? x / s : x;
 }
@@ -277,7 +278,7 @@ __global__ __launch_bounds__(256) void quant_act_dual_kernel(const uint16_t *__r
 #pragma unroll
     for (int e = 1; e < 8; ++e) m = fmaxf(m, fabsf(xv[i][e]));
     const float s = row16_max(m) / kE4M3Max;
-    *reinterpret_cast<uint2 *>(xq + base + (r0 + 16 * i) * K) = quant8f(xv[i], GroupDiv(s));
+    *reinterpret_cast<uint2 *>(xq + base + (r0 + 16 * i) * K) = quant8f<true>(xv[i], GroupDiv(s));
     if (sub == 0) sa[kb * M + mb * 128 + r0 + 16 * i] = s;
   }
 
@@ -326,7 +327,7 @@ __global__ __launch_bounds__(256) void quant_act_dual_kernel(const uint16_t *__r
         GroupDiv d(0.0f);
         d.s = cs[e];
         d.r = cr[e];
-        y[e] = d.fast(xv[i][e]);
+        y[e] = d.fast_bf16(xv[i][e]);
       } else {
         y[e] = div_any(xv[i][e], cs[e], cr[e], cmode[e]);
       }
@@ -412,7 +413,7 @@ __global__ __launch_bounds__(256) void swiglu_quant_act_1x128_kernel(const uint1
       }
       const float s = row16_max(m) / kE4M3Max;
       const int64_t row = row0 + 4 * i + grp;
-      const uint2 q = quant8f(h, GroupDiv(s));
+      const uint2 q = quant8f<false>(h, GroupDiv(s));
       if (row < M) *reinterpret_cast<uint2 *>(xq + row * I + col) = q;
       if (sub == 0 && row < M) sa[(kb0 + k) * M + row] = s;
     }
@@ -471,6 +472,10 @@ __global__ __launch_bounds__(256) void tensor_quant_kernel(const uint16_t *__res
                                                            uint8_t *__restrict__ q, uint32_t *__restrict__ stats) {
   const float s = kDelayed ? *scale_in : __uint_as_float(stats[0]) / kE4M3Max;
   const GroupDiv dv(s);
+  // A caller's scale can put |x/s| beyond the FP32 range; every quotient above 448 maps to
+  // the same saturated code, so dividends are clamped to +-512 s first (exact for a mode-1
+  // s), which keeps the fast quotient finite and makes the clamped ones exactly +-512.
+  const float lim = 512.0f * s;
   float m = 0.0f;
   uint32_t sat = 0;
   for (int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; c < chunks;
@@ -481,7 +486,8 @@ __global__ __launch_bounds__(256) void tensor_quant_kernel(const uint16_t *__res
     if (kDelayed) m = fmaxf(m, absmax8(v));
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      y[i] = dv.mode == 1 ? dv.fast(y[i]) : (dv.mode == 2 ? y[i] / dv.s : y[i]);
+      y[i] = dv.mode == 1 ? dv.fast_bf16(__builtin_amdgcn_fmed3f(y[i], -lim, lim))
+                          : (dv.mode == 2 ? y[i] / dv.s : y[i]);
       sat += fabsf(y[i]) > kE4M3Max ? 1u : 0u;
     }
     uint2 out;

@@ -15,8 +15,9 @@ Readings (the pages give no formula for either):
   of quant.quantize_group (nearest even, saturating);
 * delayed: s = RN32(max(history) / 448) with history the amax of the previous L steps
   (the current amax is not used for the current step, it is appended to the history);
-  values whose quotient exceeds 448 saturate to +-448; the number of saturated elements is
-  reported;
+  values whose quotient exceeds 448 saturate to +-448, including a quotient beyond the FP32
+  range (a stale scale far below the current values), and the number of saturated elements
+  is reported;
 * both feed the same block-scaled GEMM with every tile / block scale equal to the tensor's
   scale, so the comparison isolates the scaling granularity.
 
@@ -45,8 +46,11 @@ def delayed_quantize(x32: np.ndarray, history):
     amax = np.float32(np.max(np.abs(x)))
     if s == 0:
         return e4m3.encode(x), s, 0, amax
-    y = (x / s).astype(np.float32)
+    with np.errstate(over="ignore"):
+        y = (x / s).astype(np.float32)
     saturated = int(np.count_nonzero(np.abs(y) > np.float32(448.0)))
+    # an FP32 overflow (+-inf) saturates like any other quotient above 448
+    y = np.where(np.isinf(y), np.copysign(np.float32(2 * 448.0), y), y).astype(np.float32)
     return e4m3.encode(y), s, saturated, amax
 
 

@@ -46,6 +46,25 @@ def test_delayed_saturates_outliers():
     print(f"\n[delayed] {sat} of {x.size} values saturated (history max 1/20 of the current amax)")
 
 
+def test_delayed_quotient_beyond_fp32_range():
+    """A caller's scale of ~1e-10 against values up to 1e30: quotients from below 448 to
+    past the FP32 range (overflow), signed zeros; codes and count bit-exact."""
+    rng = np.random.default_rng(21)
+    xf = (rng.standard_normal(4096) * 3e-8).astype(np.float32)
+    xf[::97] = 1e30
+    xf[5::97] = -1e30
+    xf[7::97] = -0.0
+    xf[9::97] = 0.0
+    x = wl.bf16_bits(xf)
+    xr = oq.bf16_to_f32(x)
+    history = [float(np.float32(1e-10) * np.float32(448.0))]
+    rq, rs, rsat, ramax = oc.delayed_quantize(xr, history)
+    q, (amax, sat, s) = run(x, float(rs))
+    assert np.float32(s) == rs and np.float32(amax) == ramax
+    assert sat == rsat and 0 < sat < x.size
+    assert np.array_equal(q, rq)
+
+
 def test_zero_and_empty():
     q, (amax, sat, s) = run(np.zeros((4, 128), np.uint16))
     assert amax == 0 and s == 0 and sat == 0 and np.all(q == 0)

@@ -31,6 +31,17 @@ def test_delayed_saturation_closed_form():
     assert np.array_equal(q[[0, 1, 2, 5]], ref)
 
 
+def test_delayed_quotient_beyond_fp32_range_saturates():
+    """A stale scale far below the values: 1e30 / 1e-10 overflows FP32 and still gives the
+    saturated code and is counted; 1e-3 / 1e-10 = 1e7 saturates too; zeros keep their sign."""
+    x = np.array([1e30, -1e30, 1e-3, 0.0, -0.0], np.float32)
+    h = np.float32(np.float32(1e-10) * np.float32(448.0))
+    q, s, sat, amax = oc.delayed_quantize(x, [h])
+    assert s == np.float32(h / np.float32(448.0))
+    assert sat == 3 and amax == np.float32(1e30)
+    assert q.tolist() == [0x7E, 0xFE, 0x7E, 0x00, 0x80]
+
+
 def test_delayed_with_current_history_equals_per_tensor():
     rng = np.random.default_rng(2)
     x = rng.standard_normal(1000).astype(np.float32)
