@@ -23,11 +23,18 @@
 // fragment row and 8- or 16-byte output stores.
 //
 // Operand staging: both stages live in LDS, double buffered.  gfx950's buffer_load ... lds
-// moves 16 B per lane from global memory straight into LDS; each wave's load fills 1 KB =
-// 8 rows of 128 B.  The lane->address map applies an XOR swizzle of the 16-byte chunk
-// index with the row so the fragment reads (ds_read_b128, 16 consecutive rows of one chunk
-// column) spread over the banks.  The two buffers are separate LDS arrays, so the compiler
-// can see that reading one does not wait for the loads in flight into the other.
+// moves 16 B per lane from global memory straight into LDS, lane p's bytes landing at 16p
+// of a 1 KB block, from any global address; each group of 8 lanes fetches one 128-byte
+// K block of one row.  Layout of a stage, per group of 16 rows (2 KB): rows r and r+8 of
+// the group share a 256-byte line (r in the low half, r+8 in the high half), and the
+// 16-byte chunks of a row are XOR-swizzled by r mod 8.  A fragment read (ds_read_b128,
+// lane 16kg+r taking chunk 2kg+h of row r) then has lanes 0-7 and 8-15 of each 16-lane
+// group in opposite halves of eight different lines at eight different chunk slots; on
+// gfx950 this reads at close to the LDS's full 256 B per clock, while a row-major tile
+// (two consecutive rows per line) read in fragment shape reaches about half of that
+// whatever the swizzle, as the four 16-lane groups then collide on shared lines.  The
+// two buffers are separate LDS arrays, so the compiler can see that reading one does not
+// wait for the loads in flight into the other.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -50,10 +57,11 @@ constexpr int kGroupM = 8;  // M tiles per raster group (L2 reuse of weight pane
 #ifndef FP8Q_PRIO
 #define FP8Q_PRIO 1
 #endif
-// XOR swizzle of the 16-byte chunk index by row: rows 2i and 2i+1 go to the two 128-byte
-// halves of a 256-byte bank line and pairs i spread over the 8 chunk slots, so the 16 rows
-// of a fragment read (ds_read_b128) hit distinct banks.
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+// LDS byte offset, within its stage, of chunk c (16 bytes) of row `row` (see above).
+__device__ __forceinline__ int lds_pos(int row, int c) {
+  const int r = row & 15;
+  return (row >> 4) * 2048 + (r & 7) * 256 + (r >> 3) * 128 + ((c ^ (r & 7)) << 4);
+}
 
 // Buffer resource (gfx9 family layout) over `bytes` bytes at `p`; loads at or past the
 // end return zeros, which is how rows beyond the tile's valid range are filled.
@@ -62,18 +70,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
                                            static_cast<int>(bytes), 0x00020000);
 }
 
-// Per-lane byte offsets of the pieces a lane moves for one stage: wave w fills LDS chunks
-// c = 8*i + w (8 rows each, 1 KB); lane p of chunk c lands at LDS row 8c + p/8, slot p%8,
-// and fetches global chunk slot ^ swz(row) of that row.  Both operands use these offsets
-// (both have row stride K).
+// Per-lane byte offsets of the pieces a lane moves for one stage: wave w fills LDS blocks
+// b = 8*i + w (1 KB = 4 lines); lane p of block b lands on line 4*(b%2) + p/16, half
+// (p/8)%2, slot p%8 of row group b/2, i.e. on row 16*(b/2) + line + 8*half, chunk
+// slot ^ line of that row (the inverse of lds_pos).  Both operands use these offsets (both
+// have row stride K).
 template <int NO = 4>
 __device__ __forceinline__ void stage_offsets(int64_t K, int wave, int lane, uint32_t (&off)[NO]) {
-  const int r_in = lane >> 3;
-  const int slot = lane & 7;
 #pragma unroll
   for (int i = 0; i < NO; ++i) {
-    const int row = 8 * (8 * i + wave) + r_in;
-    off[i] = static_cast<uint32_t>(row) * static_cast<uint32_t>(K) + static_cast<uint32_t>((slot ^ swz(row)) << 4);
+    const int b = 8 * i + wave;
+    const int line = 4 * (b & 1) + (lane >> 4);
+    const int row = 16 * (b >> 1) + line + 8 * ((lane >> 3) & 1);
+    const int chunk = (lane & 7) ^ line;
+    off[i] = static_cast<uint32_t>(row) * static_cast<uint32_t>(K) + static_cast<uint32_t>(chunk << 4);
   }
 }
 
@@ -90,11 +100,12 @@ __device__ __forceinline__ void stage_load(__amdgpu_buffer_rsrc_t rsrc, const ui
                                              static_cast<int>(off[i]), static_cast<int>(koff), 0, 0);
 }
 
-// One MFMA operand fragment: row `row` of the stage, K bytes [32*kg, 32*kg + 32).
-__device__ __forceinline__ v8i frag(const FP8Q_LDS uint8_t *lds, int row, int kg) {
-  const FP8Q_LDS uint8_t *rp = lds + row * kBK;
-  const v4i lo = *reinterpret_cast<const FP8Q_LDS v4i *>(rp + (((2 * kg) ^ swz(row)) << 4));
-  const v4i hi = *reinterpret_cast<const FP8Q_LDS v4i *>(rp + (((2 * kg + 1) ^ swz(row)) << 4));
+// One MFMA operand fragment: rows 16g .. 16g+15 of the stage, lane 16kg + r taking K bytes
+// [32kg, 32kg + 32) of row 16g + r.  fo0 / fo1 = lds_pos(r, 2kg) / lds_pos(r, 2kg + 1)
+// for the lane's r and kg (row group 0).
+__device__ __forceinline__ v8i frag(const FP8Q_LDS uint8_t *lds, int g, int fo0, int fo1) {
+  const v4i lo = *reinterpret_cast<const FP8Q_LDS v4i *>(lds + g * 2048 + fo0);
+  const v4i hi = *reinterpret_cast<const FP8Q_LDS v4i *>(lds + g * 2048 + fo1);
   return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 }
 
@@ -191,6 +202,8 @@ __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(t.w + t.n0 * K, static_cast<uint32_t>(rows_w * K));
   uint32_t off[kNO];
   stage_offsets(K, wave, lane, off);
+  const int fo0 = lds_pos(l16, 2 * kg), fo1 = lds_pos(l16, 2 * kg + 1);  // fragment-read offsets
+  const int wg0 = wn * kWN / 16;  // first weight row group of this wave
 
   // activation-scale rows of this lane (one per 16-row fragment), clamped into the tile
   int srow[4];
@@ -264,9 +277,9 @@ __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict
     __syncthreads();
     // Operands of the first MFMA first, then the copies of the next stage, then the other
     // activation fragments.
-    v8i wnext = frag(cw, wn * kWN + l16, kg);
+    v8i wnext = frag(cw, wg0, fo0, fo1);
     v8i xf[4];
-    xf[0] = frag(cx, wm * 64 + l16, kg);
+    xf[0] = frag(cx, wm * 4, fo0, fo1);
     const int kn = kb + 1 < KB ? kb + 1 : kb;
     const uint32_t koff = static_cast<uint32_t>(kn) * kBK;
     stage_load<kXL>(rx, off, koff, nx, wave);
@@ -280,7 +293,7 @@ __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict
       sb1_nxt = sbrow1[kn];
     }
 #pragma unroll
-    for (int f = 1; f < 4; ++f) xf[f] = frag(cx, wm * 64 + f * 16 + l16, kg);
+    for (int f = 1; f < 4; ++f) xf[f] = frag(cx, wm * 4 + f, fo0, fo1);
 #pragma unroll
     for (int j = 0; j < NFR; ++j) {
 #if FP8Q_PRIO
@@ -291,7 +304,7 @@ __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict
       if (j == 0 || (j * 4) / NFR != ((j - 1) * 4) / NFR) set_prio(3 - (j * 4) / NFR);
 #endif
       const v8i wf = wnext;
-      if (j + 1 < NFR) wnext = frag(cw, wn * kWN + (j + 1) * 16 + l16, kg);
+      if (j + 1 < NFR) wnext = frag(cw, wg0 + j + 1, fo0, fo1);
       v4f np[4];
 #pragma unroll
       for (int f = 0; f < 4; ++f) np[f] = mfma_block(wf, xf[f]);
