@@ -410,7 +410,7 @@ def main():
     traffic = measured_traffic(args.workload)
     roofline = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
-                "kernel": "gemm_grouped_kernel" if grouped else "gemm_blockscaled_split_kernel<8, 6>",
+                "kernel": "gemm_grouped_kernel" if grouped else "gemm_blockscaled_split_kernel<8, 6, false>",
                 "flop_per_launch": flops, "avg_launch_us": round(a_g * 1e6, 2),
                 "algorithmic_bytes_per_launch": bytes_gemm}
     if grouped:
