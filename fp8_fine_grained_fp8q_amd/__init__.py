@@ -32,9 +32,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("FP8Q_LIBRARY") or os.path.join(HERE, "libfp8q.so")
 
 FP8Q_OK = 0
+FP8Q_ERR_OFFSETS = -7  # grouped GEMM offsets rejected by the FP8Q_DEBUG check
 FP8Q_OUT_BF16 = 0
 FP8Q_OUT_F32 = 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 EXPORTED = ("fp8q_quantize_act_1x128", "fp8q_quantize_w_128x128", "fp8q_gemm_blockscaled",
             "fp8q_grouped_gemm_blockscaled", "fp8q_quantize_w_128x128_t", "fp8q_quantize_act_dual",

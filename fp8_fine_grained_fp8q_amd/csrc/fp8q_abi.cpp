@@ -3,6 +3,7 @@
 #include "fp8q.h"
 
 #include <hip/hip_runtime.h>
+#include <stdlib.h>
 
 #include "fp8q_launch.h"
 
@@ -26,6 +27,12 @@ fp8q_status device_ok() {
 fp8q_status launched(hipError_t e) { return e == hipSuccess ? FP8Q_OK : FP8Q_ERR_LAUNCH; }
 
 hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+// FP8Q_DEBUG set to anything but "" or "0" turns on the synchronizing argument checks.
+bool debug_checks() {
+  const char *v = getenv("FP8Q_DEBUG");
+  return v != nullptr && v[0] != '\0' && !(v[0] == '0' && v[1] == '\0');
+}
 
 // Shared checks of the two GEMM entry points (everything except the grouped extras).
 fp8q_status check_gemm(const uint8_t *xq, const float *sa, const uint8_t *wq, const float *sb,
@@ -92,6 +99,12 @@ fp8q_status fp8q_grouped_gemm_blockscaled(const uint8_t *xq, const float *sa, co
   if (!offsets) return FP8Q_ERR_NULL;
   if (misaligned(offsets, 4)) return FP8Q_ERR_ALIGN;
   if (device_ok() != FP8Q_OK) return FP8Q_ERR_DEVICE;
+  if (debug_checks()) {
+    bool bad = false;
+    if (fp8q::check_grouped_offsets(offsets, G, M_tot, as_stream(stream), &bad) != hipSuccess)
+      return FP8Q_ERR_LAUNCH;
+    if (bad) return FP8Q_ERR_OFFSETS;
+  }
   return launched(fp8q::launch_grouped_gemm(xq, sa, wq, sb, offsets, G, M_tot, N, K, c,
                                             out_dtype == FP8Q_OUT_F32, as_stream(stream)));
 }
@@ -162,6 +175,7 @@ const char *fp8q_status_string(fp8q_status status) {
     case FP8Q_ERR_DTYPE: return "invalid out_dtype";
     case FP8Q_ERR_DEVICE: return "no usable HIP device";
     case FP8Q_ERR_LAUNCH: return "kernel launch failed";
+    case FP8Q_ERR_OFFSETS: return "grouped GEMM offsets invalid (offsets[0] != 0, decreasing, or offsets[G] != M_tot)";
     default: return "unknown status";
   }
 }

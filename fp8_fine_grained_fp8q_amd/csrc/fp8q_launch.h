@@ -35,6 +35,10 @@ hipError_t launch_gemm(const uint8_t *xq, const float *sa, const uint8_t *wq, co
 hipError_t launch_gemm_rowscaled(const uint8_t *aq, const float *sa, const uint8_t *bq, const float *sb,
                                  int64_t M, int64_t N, int64_t K, void *c, bool out_f32, hipStream_t stream);
 
+// Debug check of grouped-GEMM offsets (offsets[0] == 0, non-decreasing, offsets[G] == M_tot)
+// on `stream`; waits for the stream and sets *bad.
+hipError_t check_grouped_offsets(const int32_t *offsets, int64_t G, int64_t M_tot, hipStream_t stream, bool *bad);
+
 hipError_t launch_grouped_gemm(const uint8_t *xq, const float *sa, const uint8_t *wq, const float *sb,
                                const int32_t *offsets, int64_t G, int64_t M_tot, int64_t N, int64_t K,
                                void *c, bool out_f32, hipStream_t stream);

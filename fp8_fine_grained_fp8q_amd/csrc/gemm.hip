@@ -561,6 +561,41 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_grouped_kernel(
   }
 }
 
+// Debug check of the grouped GEMM's offsets: one workgroup scans offsets[0..G] and raises
+// a per-device flag on the first violation it sees (plain stores of the same value).
+__device__ int32_t g_offsets_bad;
+
+__global__ void offsets_flag_clear_kernel() {
+  if (threadIdx.x == 0) g_offsets_bad = 0;
+}
+
+__global__ __launch_bounds__(256) void offsets_check_kernel(const int32_t *__restrict__ offsets, int64_t G,
+                                                            int64_t M_tot) {
+  bool bad = false;
+  for (int64_t g = threadIdx.x; g <= G; g += blockDim.x) {
+    const int64_t v = offsets[g];
+    if (g == 0 && v != 0) bad = true;
+    if (g == G && v != M_tot) bad = true;
+    if (g > 0 && offsets[g - 1] > v) bad = true;
+  }
+  if (bad) g_offsets_bad = 1;
+}
+
+hipError_t check_grouped_offsets(const int32_t *offsets, int64_t G, int64_t M_tot, hipStream_t stream,
+                                 bool *bad) {
+  hipLaunchKernelGGL(offsets_flag_clear_kernel, dim3(1), dim3(64), 0, stream);
+  hipLaunchKernelGGL(offsets_check_kernel, dim3(1), dim3(256), 0, stream, offsets, G, M_tot);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if ((e = hipStreamSynchronize(stream)) != hipSuccess) return e;
+  int32_t flag = 0;
+  if ((e = hipMemcpyFromSymbol(&flag, HIP_SYMBOL(g_offsets_bad), sizeof(flag), 0, hipMemcpyDeviceToHost)) !=
+      hipSuccess)
+    return e;
+  *bad = flag != 0;
+  return hipSuccess;
+}
+
 namespace {
 
 int device_cus() {

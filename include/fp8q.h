@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define FP8Q_ABI_VERSION 4
+#define FP8Q_ABI_VERSION 5
 
 typedef int32_t fp8q_status;
 
@@ -68,7 +68,8 @@ enum {
   FP8Q_ERR_ALIGN = -3,  /* a base pointer is not 16-byte aligned                        */
   FP8Q_ERR_DTYPE = -4,  /* out_dtype is neither FP8Q_OUT_BF16 nor FP8Q_OUT_F32          */
   FP8Q_ERR_DEVICE = -5, /* no usable HIP device                                          */
-  FP8Q_ERR_LAUNCH = -6  /* the kernel launch failed (hipGetLastError)                   */
+  FP8Q_ERR_LAUNCH = -6,  /* the kernel launch failed (hipGetLastError)                  */
+  FP8Q_ERR_OFFSETS = -7  /* grouped GEMM offsets invalid (checked only under FP8Q_DEBUG) */
 };
 
 enum { FP8Q_OUT_BF16 = 0, FP8Q_OUT_F32 = 1 };
@@ -119,8 +120,13 @@ fp8q_status fp8q_gemm_blockscaled(const uint8_t *xq, const float *sa, const uint
  * experts active per token: risenshineclean.com page, section 2).
  *   xq [M_tot][K], sa [K/128][M_tot], wq [G][N][K], sb [G][N/128][K/128]
  *   offsets : DEVICE int32 [G+1]; must satisfy offsets[0] == 0, non-decreasing,
- *             offsets[G] == M_tot.  Not checked on the host (that would need a sync);
- *             the kernel clamps every range to [0, M_tot).
+ *             offsets[G] == M_tot.  Not checked by default (that needs a sync); the
+ *             kernel clamps every range to [0, M_tot).  With the environment variable
+ *             FP8Q_DEBUG set (to anything but "" or "0"; read on every call) the call
+ *             first checks them on the device, waits for `stream`, and returns
+ *             FP8Q_ERR_OFFSETS without launching the GEMM if they are invalid.  The check
+ *             uses one flag per device: debug calls on one GPU must not run concurrently
+ *             from several host threads.
  *   c [M_tot][N] (out); rows outside every expert range are left untouched.
  * Requires G >= 1, N % 128 == 0, K % 128 == 0, K >= 128, M_tot >= 0.
  */

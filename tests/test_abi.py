@@ -46,8 +46,10 @@ def test_enum_values_match_binding(lib):
     assert e["FP8Q_OK"] == fq.FP8Q_OK == 0
     assert e["FP8Q_OUT_BF16"] == fq.FP8Q_OUT_BF16 and e["FP8Q_OUT_F32"] == fq.FP8Q_OUT_F32
     assert lib.fp8q_abi_version() == fq.ABI_VERSION
-    for code in (0, -1, -2, -3, -4, -5, -6, -99):
+    assert e["FP8Q_ERR_OFFSETS"] == fq.FP8Q_ERR_OFFSETS
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -99):
         assert isinstance(fq.status_string(code), str) and fq.status_string(code)
+    assert "offsets" in fq.status_string(fq.FP8Q_ERR_OFFSETS)
 
 
 def test_quantize_act_argument_checks(lib):

@@ -228,6 +228,28 @@ def test_grouped_rows_outside_ranges_untouched():
         assert_gemm_within_tol(got[lo:hi], ref[lo:hi], xn[lo:hi], og.row_norms_w(wq[g], sb[g]), f"expert {g}")
 
 
+def test_grouped_debug_offsets_check(monkeypatch):
+    """With FP8Q_DEBUG set, valid offsets give the same result as without the check and
+    invalid ones (first != 0, decreasing, last != M_tot) return FP8Q_ERR_OFFSETS with
+    nothing written; FP8Q_DEBUG=0 turns the check off again."""
+    G, N, K, M = 3, 256, 256, 200
+    xq, sa, wq, sb = quantized(M, N, K, seed=31, G=G)
+    good = np.array([0, 60, 130, 200], np.int32)
+    plain = run_grouped(xq, sa, wq, sb, good)
+    monkeypatch.setenv("FP8Q_DEBUG", "1")
+    assert np.array_equal(run_grouped(xq, sa, wq, sb, good), plain)
+    for bad in ([1, 60, 130, 200], [0, 130, 60, 200], [0, 60, 130, 199]):
+        out = torch.full((M, N), -5.0, dtype=torch.float32, device="cuda")
+        with pytest.raises(fq.Fp8qError) as err:
+            fq.fp8q_grouped_gemm_blockscaled(dev(xq), dev(sa), dev(wq), dev(sb), dev(np.array(bad, np.int32)),
+                                             out_dtype=torch.float32, out=out)
+        assert err.value.status == fq.FP8Q_ERR_OFFSETS, bad
+        torch.cuda.synchronize()
+        assert bool(torch.all(out == -5.0)), bad
+    monkeypatch.setenv("FP8Q_DEBUG", "0")
+    run_grouped(xq, sa, wq, sb, np.array([0, 130, 60, 200], np.int32))  # clamped, no check
+
+
 @pytest.mark.parametrize("name", ["moe_up", "moe_down"])
 def test_moe_workloads_sampled(name):
     """Full-size MoE workloads (32 local experts, routed token counts).  Four experts (first,
