@@ -435,6 +435,8 @@ def main():
                    "out": cfg["out_dtype"], "buffer_sets": nsets},
         "pct_fp8_peak_step": round(value / PEAK_FP8_TFLOPS * 100, 2),
         "gemm_only_tflops": round(gemm_tflops, 1),
+        # act quant + GEMM only (weights quantized in their own, separately reported call)
+        "act_quant_plus_gemm_tflops": round(flops / (a_act + a_g) / 1e12, 1),
         "kernels_us": {"quantize_act_1x128": round(a_act * 1e6, 2), "quantize_w_128x128": round(a_w * 1e6, 2),
                        "gemm": round(a_g * 1e6, 2), "device_span_per_step": round(t_dev / K_steps * 1e6, 2)},
         "quant_GBs": {"act": round(bytes_act / a_act / 1e9, 1), "act_frac_hbm": round(bytes_act / a_act / 1e9 / PEAK_HBM_GBS, 4),
