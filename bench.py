@@ -7,6 +7,8 @@ One step = one pass of the whole path over one batch of synthetic input:
        weights change every training step, so they are quantized every step)
     3. block-scaled FP8 GEMM C = X W^T with FP32 promotion every 128 K (BF16 or FP32 out),
        grouped over experts for the MoE workloads.
+Steps 1 and 2 run as one launch (fp8q_quantize_act_w) unless --quant separate; either way
+each quantizer is also timed in its own launches after the timed steps.
 Default workload: the dense projection X[4096x7168] x W[7168x7168]^T, BF16 out.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense|large|moe_up|moe_down|moe_ffn|train]
@@ -67,6 +69,8 @@ def parse():
     ap.add_argument("--workload", default="dense", choices=sorted(WORKLOADS))
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0: enough to exceed the 256 MB cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quant", choices=("fused", "separate"), default="fused",
+                    help="quantize X and W in one launch (fp8q_quantize_act_w) or in two")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy per step (untimed) for counter calibration")
     return ap.parse_args()
@@ -360,9 +364,25 @@ def main():
 
     stream = torch.cuda.current_stream()
 
+    fused = args.quant == "fused"
+
+    def quantize(s, ev=None):
+        # ev: events recorded after the activation and after the weight quantization
+        if fused:
+            fq.fp8q_quantize_act_w(s["x"], s["w"], xq=s["xq"], sa=s["sa"], wq=s["wq"], sb=s["sb"], stream=stream)
+            if ev is not None:
+                ev[0].record(stream)
+                ev[1].record(stream)
+        else:
+            fq.fp8q_quantize_act_1x128(s["x"], xq=s["xq"], sa=s["sa"], stream=stream)
+            if ev is not None:
+                ev[0].record(stream)
+            fq.fp8q_quantize_w_128x128(s["w"], wq=s["wq"], sb=s["sb"], stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+
     def step(s):
-        fq.fp8q_quantize_act_1x128(s["x"], xq=s["xq"], sa=s["sa"], stream=stream)
-        fq.fp8q_quantize_w_128x128(s["w"], wq=s["wq"], sb=s["sb"], stream=stream)
+        quantize(s)
         if grouped:
             fq.fp8q_grouped_gemm_blockscaled(s["xq"], s["sa"], s["wq"], s["sb"], off_d, out=s["c"], stream=stream)
         else:
@@ -382,10 +402,7 @@ def main():
         s = sets[i % nsets]
         e = evs[i]
         e[0].record(stream)
-        fq.fp8q_quantize_act_1x128(s["x"], xq=s["xq"], sa=s["sa"], stream=stream)
-        e[1].record(stream)
-        fq.fp8q_quantize_w_128x128(s["w"], wq=s["wq"], sb=s["sb"], stream=stream)
-        e[2].record(stream)
+        quantize(s, (e[1], e[2]))
         if grouped:
             fq.fp8q_grouped_gemm_blockscaled(s["xq"], s["sa"], s["wq"], s["sb"], off_d, out=s["c"], stream=stream)
         else:
@@ -397,6 +414,20 @@ def main():
         for _ in range(3):
             cal_dst.copy_(cal_src)
         torch.cuda.synchronize()
+
+    # Outside the timed region: each quantizer in its own launch, for the per-quantizer
+    # figures (in fused mode the timed steps run them as one launch).
+    sep = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(10)]
+    for i, e in enumerate(sep):
+        s = sets[i % nsets]
+        e[0].record(stream)
+        fq.fp8q_quantize_act_1x128(s["x"], xq=s["xq"], sa=s["sa"], stream=stream)
+        e[1].record(stream)
+        fq.fp8q_quantize_w_128x128(s["w"], wq=s["wq"], sb=s["sb"], stream=stream)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    s_act = float(np.mean([e[0].elapsed_time(e[1]) for e in sep])) * 1e-3
+    s_w = float(np.mean([e[1].elapsed_time(e[2]) for e in sep])) * 1e-3
 
     t_act = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in range(K_steps)]) * 1e-3
     t_w = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in range(K_steps)]) * 1e-3
@@ -435,12 +466,18 @@ def main():
                    "out": cfg["out_dtype"], "buffer_sets": nsets},
         "pct_fp8_peak_step": round(value / PEAK_FP8_TFLOPS * 100, 2),
         "gemm_only_tflops": round(gemm_tflops, 1),
-        # act quant + GEMM only (weights quantized in their own, separately reported call)
-        "act_quant_plus_gemm_tflops": round(flops / (a_act + a_g) / 1e12, 1),
-        "kernels_us": {"quantize_act_1x128": round(a_act * 1e6, 2), "quantize_w_128x128": round(a_w * 1e6, 2),
-                       "gemm": round(a_g * 1e6, 2), "device_span_per_step": round(t_dev / K_steps * 1e6, 2)},
-        "quant_GBs": {"act": round(bytes_act / a_act / 1e9, 1), "act_frac_hbm": round(bytes_act / a_act / 1e9 / PEAK_HBM_GBS, 4),
-                      "w": round(bytes_w / a_w / 1e9, 1), "w_frac_hbm": round(bytes_w / a_w / 1e9 / PEAK_HBM_GBS, 4)},
+        # act quant (its own launch) + GEMM only, the weights quantized in a separate call
+        "act_quant_plus_gemm_tflops": round(flops / (s_act + a_g) / 1e12, 1),
+        "quant": args.quant,
+        "kernels_us": ({"quantize_act_w (fused)": round(a_act * 1e6, 2)} if fused else
+                       {"quantize_act_1x128": round(a_act * 1e6, 2), "quantize_w_128x128": round(a_w * 1e6, 2)})
+        | {"gemm": round(a_g * 1e6, 2), "device_span_per_step": round(t_dev / K_steps * 1e6, 2),
+           "separate launches, untimed: quantize_act_1x128": round(s_act * 1e6, 2),
+           "separate launches, untimed: quantize_w_128x128": round(s_w * 1e6, 2)},
+        "quant_GBs": ({"act_w": round((bytes_act + bytes_w) / a_act / 1e9, 1),
+                       "act_w_frac_hbm": round((bytes_act + bytes_w) / a_act / 1e9 / PEAK_HBM_GBS, 4)} if fused else {})
+        | {"act": round(bytes_act / s_act / 1e9, 1), "act_frac_hbm": round(bytes_act / s_act / 1e9 / PEAK_HBM_GBS, 4),
+           "w": round(bytes_w / s_w / 1e9, 1), "w_frac_hbm": round(bytes_w / s_w / 1e9 / PEAK_HBM_GBS, 4)},
         "roofline": roofline,
         "cpu_baseline": None,
     }

@@ -8,6 +8,7 @@ missing or no GPU is present the calls raise.
 
     xq, sa = fp8q_quantize_act_1x128(x)            # x: bf16 [M, K] on cuda
     wq, sb = fp8q_quantize_w_128x128(w)            # w: bf16 [G, N, K] or [N, K]
+    xq, sa, wq, sb = fp8q_quantize_act_w(x, w)     # both in one launch
     c = fp8q_gemm_blockscaled(xq, sa, wq, sb)      # bf16 [M, N] (or out_dtype=torch.float32)
     c = fp8q_grouped_gemm_blockscaled(xq, sa, wq, sb, offsets)   # offsets: int32 [G+1] on cuda
 
@@ -35,12 +36,12 @@ FP8Q_OK = 0
 FP8Q_ERR_OFFSETS = -7  # grouped GEMM offsets rejected by the FP8Q_DEBUG check
 FP8Q_OUT_BF16 = 0
 FP8Q_OUT_F32 = 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 EXPORTED = ("fp8q_quantize_act_1x128", "fp8q_quantize_w_128x128", "fp8q_gemm_blockscaled",
             "fp8q_grouped_gemm_blockscaled", "fp8q_quantize_w_128x128_t", "fp8q_quantize_act_dual",
             "fp8q_gemm_rowscaled", "fp8q_swiglu_quantize_act_1x128", "fp8q_quantize_per_tensor",
-            "fp8q_status_string", "fp8q_abi_version")
+            "fp8q_quantize_act_w", "fp8q_status_string", "fp8q_abi_version")
 
 
 class Fp8qError(RuntimeError):
@@ -71,9 +72,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp8q_gemm_rowscaled.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i32, vp]
     lib.fp8q_swiglu_quantize_act_1x128.argtypes = [vp, i64, i64, vp, vp, vp]
     lib.fp8q_quantize_per_tensor.argtypes = [vp, i64, vp, vp, vp, vp]
+    lib.fp8q_quantize_act_w.argtypes = [vp, i64, vp, i64, i64, i64, vp, vp, vp, vp, vp]
     for name in ("fp8q_quantize_act_1x128", "fp8q_quantize_w_128x128", "fp8q_gemm_blockscaled",
                  "fp8q_grouped_gemm_blockscaled", "fp8q_quantize_w_128x128_t", "fp8q_quantize_act_dual",
-                 "fp8q_gemm_rowscaled", "fp8q_swiglu_quantize_act_1x128", "fp8q_quantize_per_tensor"):
+                 "fp8q_gemm_rowscaled", "fp8q_swiglu_quantize_act_1x128", "fp8q_quantize_per_tensor",
+                 "fp8q_quantize_act_w"):
         getattr(lib, name).restype = i32
     lib.fp8q_status_string.argtypes = [i32]
     lib.fp8q_status_string.restype = ctypes.c_char_p
@@ -145,6 +148,38 @@ def fp8q_quantize_w_128x128(w: torch.Tensor, wq: torch.Tensor | None = None,
     _check(load_library().fp8q_quantize_w_128x128(_ptr(w), G, N, K, _ptr(wq), _ptr(sb), _stream(stream)),
            "fp8q_quantize_w_128x128")
     return wq, sb
+
+
+def fp8q_quantize_act_w(x: torch.Tensor, w: torch.Tensor, xq: torch.Tensor | None = None,
+                        sa: torch.Tensor | None = None, wq: torch.Tensor | None = None,
+                        sb: torch.Tensor | None = None, stream=None):
+    """Both quantizers of a linear layer in one launch: x [M, K] -> (xq, sa) as
+    fp8q_quantize_act_1x128 and w [G, N, K] (or [N, K]) -> (wq, sb) as fp8q_quantize_w_128x128."""
+    _need(x, torch.bfloat16, "x")
+    _need(w, torch.bfloat16, "w")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    M, K = x.shape
+    squeeze = w.dim() == 2
+    G, N, Kw = (1, *w.shape) if squeeze else w.shape
+    if Kw != K:
+        raise ValueError(f"x and w must share K, got {K} and {Kw}")
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if sa is None:
+        sa = torch.empty((K // 128, M), dtype=torch.float32, device=x.device)
+    if wq is None:
+        wq = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    sb_shape = (N // 128, K // 128) if squeeze else (G, N // 128, K // 128)
+    if sb is None:
+        sb = torch.empty(sb_shape, dtype=torch.float32, device=w.device)
+    _need(xq, torch.uint8, "xq", (M, K))
+    _need(sa, torch.float32, "sa", (K // 128, M))
+    _need(wq, torch.uint8, "wq", w.shape)
+    _need(sb, torch.float32, "sb", sb_shape)
+    _check(load_library().fp8q_quantize_act_w(_ptr(x), M, _ptr(w), G, N, K, _ptr(xq), _ptr(sa), _ptr(wq), _ptr(sb),
+                                              _stream(stream)), "fp8q_quantize_act_w")
+    return xq, sa, wq, sb
 
 
 def _out_code(out_dtype) -> int:

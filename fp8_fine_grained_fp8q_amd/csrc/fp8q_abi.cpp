@@ -109,6 +109,22 @@ fp8q_status fp8q_grouped_gemm_blockscaled(const uint8_t *xq, const float *sa, co
                                             out_dtype == FP8Q_OUT_F32, as_stream(stream)));
 }
 
+fp8q_status fp8q_quantize_act_w(const uint16_t *x_bf16, int64_t M, const uint16_t *w_bf16, int64_t G, int64_t N,
+                                int64_t K, uint8_t *xq, float *sa, uint8_t *wq, float *sb, void *stream) {
+  if (bad_dim(M) || bad_dim(K) || K % 128 != 0 || too_many(M, K)) return FP8Q_ERR_SHAPE;
+  if (G < 1 || bad_dim(G) || bad_dim(N) || N % 128 != 0) return FP8Q_ERR_SHAPE;
+  if (too_many(G, N) || too_many(G * N, K)) return FP8Q_ERR_SHAPE;
+  const bool act = M > 0 && K > 0, wts = N > 0 && K > 0;
+  if (!act && !wts) return FP8Q_OK;
+  if (act && (!x_bf16 || !xq || !sa)) return FP8Q_ERR_NULL;
+  if (wts && (!w_bf16 || !wq || !sb)) return FP8Q_ERR_NULL;
+  if (act && (misaligned(x_bf16) || misaligned(xq) || misaligned(sa))) return FP8Q_ERR_ALIGN;
+  if (wts && (misaligned(w_bf16) || misaligned(wq) || misaligned(sb))) return FP8Q_ERR_ALIGN;
+  if (device_ok() != FP8Q_OK) return FP8Q_ERR_DEVICE;
+  return launched(fp8q::launch_quant_act_w(x_bf16, act ? M : 0, xq, sa, w_bf16, G, wts ? N : 0, wq, sb, K,
+                                           as_stream(stream)));
+}
+
 fp8q_status fp8q_quantize_w_128x128_t(const uint16_t *w_bf16, int64_t G, int64_t N, int64_t K,
                                       uint8_t *wq, float *sb, uint8_t *wqt, float *sbt, void *stream) {
   if (G < 1 || bad_dim(G) || bad_dim(N) || bad_dim(K)) return FP8Q_ERR_SHAPE;

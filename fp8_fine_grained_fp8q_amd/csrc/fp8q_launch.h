@@ -10,6 +10,10 @@ namespace fp8q {
 hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, uint8_t *xq, float *sa,
                             hipStream_t stream);
 
+// launch_quant_act and launch_quant_w (no W^T) for X[M][K] and W[G][N][K] in one launch.
+hipError_t launch_quant_act_w(const uint16_t *x, int64_t M, uint8_t *xq, float *sa, const uint16_t *w, int64_t G,
+                              int64_t N, uint8_t *wq, float *sb, int64_t K, hipStream_t stream);
+
 // wqt / sbt (W^T codes and block scales) are written too unless wqt is null.
 hipError_t launch_quant_w(const uint16_t *w, int64_t G, int64_t N, int64_t K, uint8_t *wq, float *sb,
                           uint8_t *wqt, float *sbt, hipStream_t stream);

@@ -37,13 +37,12 @@ namespace fp8q {
 #endif
 constexpr int kActWavesPerBlock = 4;
 
+// The activation quantizer's work for workgroup `block` (of act_blocks(M, K) in all).
 template <int NR, int NK>
-__global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t *__restrict__ x,
-                                                              int64_t M, int64_t K,
-                                                              uint8_t *__restrict__ xq,
-                                                              float *__restrict__ sa) {
+__device__ __forceinline__ void quant_act_block(int64_t block, const uint16_t *__restrict__ x, int64_t M,
+                                                int64_t K, uint8_t *__restrict__ xq, float *__restrict__ sa) {
   const int lane = threadIdx.x & 63;
-  const int64_t wave = static_cast<int64_t>(blockIdx.x) * kActWavesPerBlock + (threadIdx.x >> 6);
+  const int64_t wave = block * kActWavesPerBlock + (threadIdx.x >> 6);
   const int64_t KB = K >> 7;
   const int64_t KG = (KB + NK - 1) / NK;  // K-block groups per row slab
   const int64_t kb0 = (wave % KG) * NK;
@@ -93,12 +92,26 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t *__
   }
 }
 
-hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, uint8_t *xq, float *sa,
-                            hipStream_t stream) {
+template <int NR, int NK>
+__global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t *__restrict__ x,
+                                                              int64_t M, int64_t K,
+                                                              uint8_t *__restrict__ xq,
+                                                              float *__restrict__ sa) {
+  quant_act_block<NR, NK>(blockIdx.x, x, M, K, xq, sa);
+}
+
+// Workgroups of the activation quantizer for X[M][K].
+int64_t act_blocks(int64_t M, int64_t K) {
   constexpr int NR = FP8Q_ACT_NR, NK = FP8Q_ACT_NK;
   const int64_t KB = K / 128;
   const int64_t waves = ((M + 4 * NR - 1) / (4 * NR)) * ((KB + NK - 1) / NK);
-  const int64_t blocks = (waves + kActWavesPerBlock - 1) / kActWavesPerBlock;
+  return (waves + kActWavesPerBlock - 1) / kActWavesPerBlock;
+}
+
+hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, uint8_t *xq, float *sa,
+                            hipStream_t stream) {
+  constexpr int NR = FP8Q_ACT_NR, NK = FP8Q_ACT_NK;
+  const int64_t blocks = act_blocks(M, K);
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((quant_act_1x128_kernel<NR, NK>), dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
                      stream, x, M, K, xq, sa);
@@ -152,17 +165,14 @@ __device__ __forceinline__ void store_transposed_tile(const uint32_t *tile, uint
     *reinterpret_cast<uint4 *>(dst + (4 * kd + j) * ld + n0) = make_uint4(out[j][0], out[j][1], out[j][2], out[j][3]);
 }
 
+// The weight quantizer's work for block `bid` (= (g*N/128 + nb)*K/128 + kb).
 template <bool kTrans>
-__global__ __launch_bounds__(256) void quant_w_128x128_kernel(const uint16_t *__restrict__ w,
-                                                              int64_t N, int64_t K,
-                                                              uint8_t *__restrict__ wq,
-                                                              float *__restrict__ sb,
-                                                              uint8_t *__restrict__ wqt,
-                                                              float *__restrict__ sbt) {
+__device__ __forceinline__ void quant_w_block(int64_t bid, const uint16_t *__restrict__ w, int64_t N, int64_t K,
+                                              uint8_t *__restrict__ wq, float *__restrict__ sb,
+                                              uint8_t *__restrict__ wqt, float *__restrict__ sbt) {
   __shared__ float wave_max[4];
   __shared__ __attribute__((aligned(16))) uint32_t tile[kTrans ? 128 * 32 : 1];
   const int64_t KB = K >> 7, NB = N >> 7;
-  const int64_t bid = blockIdx.x;
   const int64_t kb = bid % KB;
   const int64_t gnb = bid / KB;  // g * NB + nb
   const int tid = threadIdx.x;
@@ -197,6 +207,42 @@ __global__ __launch_bounds__(256) void quant_w_128x128_kernel(const uint16_t *__
     __syncthreads();
     store_transposed_tile(tile, wqt + (g * K + kb * 128) * N + nb * 128, N, tid);
   }
+}
+
+template <bool kTrans>
+__global__ __launch_bounds__(256) void quant_w_128x128_kernel(const uint16_t *__restrict__ w,
+                                                              int64_t N, int64_t K,
+                                                              uint8_t *__restrict__ wq,
+                                                              float *__restrict__ sb,
+                                                              uint8_t *__restrict__ wqt,
+                                                              float *__restrict__ sbt) {
+  quant_w_block<kTrans>(blockIdx.x, w, N, K, wq, sb, wqt, sbt);
+}
+
+// Both quantizers of a linear layer in one launch: workgroups [0, w_blocks) take the
+// weight blocks, the rest the activation slabs (the shorter activation work fills the tail
+// of the weight work, and the layer pays one kernel boundary instead of two).  Each
+// workgroup does exactly what it does in its own kernel, so the outputs are identical.
+__global__ __launch_bounds__(256) void quant_act_w_kernel(const uint16_t *__restrict__ x, int64_t M,
+                                                          uint8_t *__restrict__ xq, float *__restrict__ sa,
+                                                          const uint16_t *__restrict__ w, int64_t N,
+                                                          uint8_t *__restrict__ wq, float *__restrict__ sb,
+                                                          int64_t K, int64_t w_blocks) {
+  if (static_cast<int64_t>(blockIdx.x) < w_blocks)
+    quant_w_block<false>(blockIdx.x, w, N, K, wq, sb, nullptr, nullptr);
+  else
+    quant_act_block<FP8Q_ACT_NR, FP8Q_ACT_NK>(blockIdx.x - w_blocks, x, M, K, xq, sa);
+}
+
+hipError_t launch_quant_act_w(const uint16_t *x, int64_t M, uint8_t *xq, float *sa, const uint16_t *w, int64_t G,
+                              int64_t N, uint8_t *wq, float *sb, int64_t K, hipStream_t stream) {
+  const int64_t wb = G * (N / 128) * (K / 128);
+  const int64_t total = wb + act_blocks(M, K);
+  if (total > 0x7fffffff) return hipErrorInvalidValue;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(quant_act_w_kernel, dim3(static_cast<uint32_t>(total)), dim3(256), 0, stream, x, M, xq, sa, w,
+                     N, wq, sb, K, wb);
+  return hipGetLastError();
 }
 
 hipError_t launch_quant_w(const uint16_t *w, int64_t G, int64_t N, int64_t K, uint8_t *wq, float *sb,

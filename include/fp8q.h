@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define FP8Q_ABI_VERSION 5
+#define FP8Q_ABI_VERSION 6
 
 typedef int32_t fp8q_status;
 
@@ -134,6 +134,18 @@ fp8q_status fp8q_grouped_gemm_blockscaled(const uint8_t *xq, const float *sa, co
                                           const float *sb, const int32_t *offsets, int64_t G,
                                           int64_t M_tot, int64_t N, int64_t K, void *c,
                                           int32_t out_dtype, void *stream);
+
+/*
+ * Both online quantizers of a linear layer Y = X W^T in one launch: exactly
+ * fp8q_quantize_act_1x128(x_bf16, M, K, xq, sa) and fp8q_quantize_w_128x128(w_bf16, G, N, K,
+ * wq, sb) (same sources, same bit-exact outputs), with one kernel boundary instead of two.
+ *   x_bf16 [M][K] -> xq [M][K], sa [K/128][M];  w_bf16 [G][N][K] -> wq, sb [G][N/128][K/128]
+ * Either part may be empty (M == 0, or N == 0); its pointers are then not used.
+ * Errors: FP8Q_ERR_SHAPE (K or N not a multiple of 128, G < 1, overflow), FP8Q_ERR_NULL,
+ * FP8Q_ERR_ALIGN (all six pointers 16-byte), FP8Q_ERR_DEVICE, FP8Q_ERR_LAUNCH.
+ */
+fp8q_status fp8q_quantize_act_w(const uint16_t *x_bf16, int64_t M, const uint16_t *w_bf16, int64_t G, int64_t N,
+                                int64_t K, uint8_t *xq, float *sa, uint8_t *wq, float *sb, void *stream);
 
 /*
  * Backward pass of a linear layer Y = X W^T in the same E4M3 format.  Source: the

@@ -151,6 +151,22 @@ def test_per_tensor_quantizer_argument_checks(lib):
     assert f(A, 64, A + 2, A, A, None) == E["FP8Q_ERR_ALIGN"]
 
 
+def test_fused_quantizer_argument_checks(lib):
+    r = lib.fp8q_quantize_act_w
+    A = ALIGNED
+    E = header_enums()
+    assert r(A, 4, A, 1, 128, 100, A, A, A, A, None) == E["FP8Q_ERR_SHAPE"]    # K % 128
+    assert r(A, 4, A, 1, 100, 128, A, A, A, A, None) == E["FP8Q_ERR_SHAPE"]    # N % 128
+    assert r(A, 4, A, 0, 128, 128, A, A, A, A, None) == E["FP8Q_ERR_SHAPE"]    # G < 1
+    assert r(A, -1, A, 1, 128, 128, A, A, A, A, None) == E["FP8Q_ERR_SHAPE"]
+    assert r(0, 0, A, 1, 0, 128, 0, 0, 0, 0, None) == E["FP8Q_OK"]            # nothing to do
+    assert r(0, 4, A, 1, 128, 128, A, A, A, A, None) == E["FP8Q_ERR_NULL"]     # x
+    assert r(A, 4, 0, 1, 128, 128, A, A, A, A, None) == E["FP8Q_ERR_NULL"]     # w
+    assert r(A, 4, A, 1, 128, 128, A, A, A, 0, None) == E["FP8Q_ERR_NULL"]     # sb
+    assert r(A + 4, 4, A, 1, 128, 128, A, A, A, A, None) == E["FP8Q_ERR_ALIGN"]
+    assert r(A, 4, A, 1, 128, 128, A, A, A + 8, A, None) == E["FP8Q_ERR_ALIGN"]
+
+
 def test_valid_call_without_gpu_reports_device_error(lib):
     """On a host without a GPU a well-formed call must fail cleanly, not crash."""
     import torch
@@ -159,6 +175,8 @@ def test_valid_call_without_gpu_reports_device_error(lib):
     E = header_enums()
     A = ALIGNED
     assert lib.fp8q_quantize_act_1x128(A, 4, 128, A, A, None) in (E["FP8Q_ERR_DEVICE"], E["FP8Q_ERR_LAUNCH"])
+    # the fused quantizer with an empty X needs no x / xq / sa
+    assert lib.fp8q_quantize_act_w(A, 0, A, 1, 128, 128, 0, 0, A, A, None) == E["FP8Q_ERR_DEVICE"]
 
 
 def test_binding_refuses_cpu_tensors():

@@ -2,7 +2,9 @@
 
 Inputs are the seeded workloads (tiny and dense at full size) plus constructed tiles that
 cover every BF16 value against a spread of scales (both division paths of the kernel),
-zero / signed-zero / subnormal / power-of-two / constant groups and ragged row counts."""
+zero / signed-zero / subnormal / power-of-two / constant groups and ragged row counts; the
+fused entry point (both quantizers in one launch) against the oracle and against the two
+separate launches."""
 import numpy as np
 import pytest
 import torch
@@ -139,3 +141,32 @@ def test_w_dense_full_size():
     w = wl.dense()["w"]
     wq, sb = run_w(w)
     assert_quant_equal(wq, sb, *oq.quantize_w_128x128(w), what="dense weights 7168x7168")
+
+
+@pytest.mark.parametrize("M,G,N,K", [(17, 1, 256, 384), (300, 3, 128, 640), (0, 2, 256, 256), (33, 1, 0, 512)])
+def test_fused_act_w_matches_oracle(M, G, N, K):
+    """Both quantizers in one launch: the same codes and scales as the oracle (ragged rows,
+    several experts, and each half empty in turn)."""
+    rng = np.random.default_rng(M * 7 + G * 5 + N + K)
+    x = wl.bf16_bits(rng.standard_normal((M, K), dtype=np.float32) * np.float32(3.0))
+    w = wl.bf16_bits(rng.standard_normal((G, N, K), dtype=np.float32) * np.float32(0.02))
+    xq, sa, wq, sb = fq.fp8q_quantize_act_w(dev_bf16(x), dev_bf16(w))
+    torch.cuda.synchronize()
+    if M:
+        assert_quant_equal(xq, sa, *oq.quantize_act_1x128(x), what=f"fused act {M}x{K}")
+    if N:
+        assert_quant_equal(wq, sb, *oq.quantize_w_128x128(w), what=f"fused weights {G}x{N}x{K}")
+
+
+def test_fused_act_w_equals_separate_calls_full_size():
+    """At the dense workload's full size the fused launch writes exactly what the two
+    separate quantizer launches write."""
+    c = wl.dense()
+    x, w = dev_bf16(c["x"]), dev_bf16(c["w"][0])
+    xq1, sa1 = fq.fp8q_quantize_act_1x128(x)
+    wq1, sb1 = fq.fp8q_quantize_w_128x128(w)
+    xq2, sa2, wq2, sb2 = fq.fp8q_quantize_act_w(x, w)
+    torch.cuda.synchronize()
+    assert torch.equal(xq1, xq2) and torch.equal(wq1, wq2)
+    assert torch.equal(sa1.view(torch.int32), sa2.view(torch.int32))
+    assert torch.equal(sb1.view(torch.int32), sb2.view(torch.int32))
