@@ -40,6 +40,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "fp8q_launch.h"
 
 namespace fp8q {
@@ -268,8 +270,15 @@ __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict
     sclp[f] = 0.0f;
     sa_prev[f] = 0.0f;
   }
-  auto step = [&](const FP8Q_LDS uint8_t *cx, const FP8Q_LDS uint8_t *cw, FP8Q_LDS uint8_t *nx,
+  // kOne (block-scaled B only): all of this wave's columns lie in one 128-column scale
+  // block, so a fragment's scale is the same for every column of the step: sa*sb is
+  // formed once per step instead of once per column.
+  auto step = [&](auto one_block, const FP8Q_LDS uint8_t *cx, const FP8Q_LDS uint8_t *cw, FP8Q_LDS uint8_t *nx,
                   FP8Q_LDS uint8_t *nw, const FP8Q_LDS uint8_t *csc, FP8Q_LDS uint8_t *nsc, int kb) {
+    constexpr bool kOne = decltype(one_block)::value;
+    float scl0[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) scl0[f] = kOne ? sa_cur[f] * sb0_cur : 0.0f;
     // Stage kb has landed in LDS once every wave's own copies are done (vmcnt(0) before
     // the barrier: the compiler's fence does not count direct-to-LDS loads), and after
     // the barrier every wave is also done reading the other buffer.
@@ -324,7 +333,7 @@ __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict
         const float sbj = jp < jsplit ? sb0_cur : sb1_cur;  // wave-uniform
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
-          const float sc = j == 0 ? sclp[f] : sa_cur[f] * sbj;
+          const float sc = j == 0 ? sclp[f] : (kOne ? scl0[f] : sa_cur[f] * sbj);
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[f][jp][i] = __builtin_fmaf(pp[f][i], sc, acc[f][jp][i]);
           pp[f] = np[f];
@@ -352,12 +361,18 @@ __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict
     sb1_cur = sb1_nxt;
   };
 
-  int kb = 0;
-  for (; kb + 1 < KB; kb += 2) {
-    step(st.x0, st.w0, st.x1, st.w1, st.c0, st.c1, kb);
-    step(st.x1, st.w1, st.x0, st.w0, st.c1, st.c0, kb + 1);
-  }
-  if (kb < KB) step(st.x0, st.w0, st.x1, st.w1, st.c0, st.c1, kb);
+  auto kloop = [&](auto one_block) {
+    int kb = 0;
+    for (; kb + 1 < KB; kb += 2) {
+      step(one_block, st.x0, st.w0, st.x1, st.w1, st.c0, st.c1, kb);
+      step(one_block, st.x1, st.w1, st.x0, st.w0, st.c1, st.c0, kb + 1);
+    }
+    if (kb < KB) step(one_block, st.x0, st.w0, st.x1, st.w1, st.c0, st.c1, kb);
+  };
+  if (!kRowB && jsplit >= NFR)
+    kloop(std::integral_constant<bool, !kRowB>{});
+  else
+    kloop(std::false_type{});
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the last (repeated) copy
 #pragma unroll
   for (int f = 0; f < 4; ++f)
