@@ -38,5 +38,6 @@ Modules:
               token tiles, the GEMM with per-row scales on both operands
     swiglu -- SwiGLU of the expert up-projection output followed by the 1x128 quantizer
     comparators -- tensor-level and delayed (historical-max) scaling, for the accuracy study
+    moe    -- expert-parallel dispatch (expert-sorted rows of codes and scales) and combine
 """
-from . import e4m3, quant, gemm, backward, swiglu, comparators  # noqa: F401
+from . import e4m3, quant, gemm, backward, swiglu, comparators, moe  # noqa: F401

@@ -90,17 +90,27 @@ def dense(seed: int = SEEDS["dense"], M: int = 4096, N: int = 7168, K: int = 716
             "outlier_channels": np.sort(ch)}
 
 
-def routing(seed: int = SEEDS["moe_up"], tokens: int = 8192, experts: int = 256, topk: int = 8,
-            local: int = 32, bias_std: float = 0.003):
-    """Top-8-of-256 routing from N(0,1) logits, softmax scores plus a static per-expert bias
-    (used for selection only), ties to the lower expert index.  Returns, for the first
-    ``local`` experts, the token ids routed to each (ascending) and the offsets array."""
+def topk_routing(seed: int = SEEDS["moe_up"], tokens: int = 8192, experts: int = 256, topk: int = 8,
+                 bias_std: float = 0.003):
+    """Top-8-of-256 routing from N(0,1) logits: softmax scores plus a static per-expert bias
+    (used for selection only), ties to the lower expert index.  Returns the selected expert
+    ids [tokens][topk] (int32, by decreasing biased score) and their gating weights (the
+    unbiased scores of the selected experts normalised to sum to 1 per token, float32)."""
     r_logit, r_bias = _rngs(seed + 100, 2)
     logits = r_logit.standard_normal((tokens, experts))
     e = np.exp(logits - logits.max(axis=1, keepdims=True))
     score = e / e.sum(axis=1, keepdims=True)
     bias = bias_std * r_bias.standard_normal(experts)
     sel = np.argsort(-(score + bias), axis=1, kind="stable")[:, :topk]
+    g = np.take_along_axis(score, sel, axis=1)
+    return sel.astype(np.int32), (g / g.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
+def routing(seed: int = SEEDS["moe_up"], tokens: int = 8192, experts: int = 256, topk: int = 8,
+            local: int = 32, bias_std: float = 0.003):
+    """For the first ``local`` experts of topk_routing: the token ids routed to each
+    (ascending) and the offsets array."""
+    sel, _ = topk_routing(seed, tokens, experts, topk, bias_std)
     rows = []
     for g in range(local):
         rows.append(np.nonzero((sel == g).any(axis=1))[0].astype(np.int64))
@@ -141,6 +151,20 @@ def large(seed: int = SEEDS["large"], M: int = 16384, N: int = 18432, K: int = 7
     return {"name": "large", "x": bf16_bits(x), "w": w, "offsets": None, "out_dtype": "f32"}
 
 
+def moe_layer(seed: int = SEEDS["moe_up"], tokens: int = 8192, hidden: int = 7168, inter: int = 2048,
+              local: int = 32):
+    """One GPU's share of the MoE expert layer from the token side: the moe_up tokens in
+    token order X[tokens][hidden], their top-8 routing (global expert ids and gating
+    weights), and the 32 local experts' W_up[32][2*inter x hidden] and W_down[32][hidden x inter]."""
+    ids, gate = topk_routing(seed, tokens=tokens)
+    r_x, = _rngs(seed, 1)
+    x = bf16_bits(r_x.standard_normal((tokens, hidden), dtype=np.float32))
+    w_up = _weights(_rngs(seed * 1000 + 7, local), local, 2 * inter, hidden)
+    w_down = _weights(_rngs(SEEDS["moe_down"] * 1000 + 7, local), local, hidden, inter)
+    return {"name": "moe_layer", "x": x, "topk_ids": ids, "topk_w": gate, "e_begin": 0, "local": local,
+            "w": w_up, "w_down": w_down, "offsets": None, "out_dtype": "bf16"}
+
+
 def moe_ffn(seed: int = SEEDS["moe_up"]):
     """The expert FFN forward of the 32 local experts: the moe_up input and up-projection
     weights plus the moe_down workload's down-projection weights W_down[32][7168x2048]."""
@@ -165,4 +189,4 @@ def train(seed: int = SEEDS["train"], M: int = 4096, N: int = 7168, K: int = 716
 
 
 CONFIGS = {"tiny": tiny, "dense": dense, "moe_up": moe_up, "moe_down": moe_down, "large": large, "train": train,
-           "moe_ffn": moe_ffn}
+           "moe_ffn": moe_ffn, "moe_layer": moe_layer}
