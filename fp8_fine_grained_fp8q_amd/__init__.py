@@ -36,12 +36,13 @@ FP8Q_OK = 0
 FP8Q_ERR_OFFSETS = -7  # grouped GEMM offsets rejected by the FP8Q_DEBUG check
 FP8Q_OUT_BF16 = 0
 FP8Q_OUT_F32 = 1
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 EXPORTED = ("fp8q_quantize_act_1x128", "fp8q_quantize_w_128x128", "fp8q_gemm_blockscaled",
             "fp8q_grouped_gemm_blockscaled", "fp8q_quantize_w_128x128_t", "fp8q_quantize_act_dual",
             "fp8q_gemm_rowscaled", "fp8q_swiglu_quantize_act_1x128", "fp8q_quantize_per_tensor",
-            "fp8q_quantize_act_w", "fp8q_status_string", "fp8q_abi_version")
+            "fp8q_quantize_act_w", "fp8q_moe_dispatch", "fp8q_moe_combine", "fp8q_status_string",
+            "fp8q_abi_version")
 
 
 class Fp8qError(RuntimeError):
@@ -73,10 +74,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp8q_swiglu_quantize_act_1x128.argtypes = [vp, i64, i64, vp, vp, vp]
     lib.fp8q_quantize_per_tensor.argtypes = [vp, i64, vp, vp, vp, vp]
     lib.fp8q_quantize_act_w.argtypes = [vp, i64, vp, i64, i64, i64, vp, vp, vp, vp, vp]
+    lib.fp8q_moe_dispatch.argtypes = [vp, i64, i64, i64, i64, vp, vp, i64, i64, vp, vp, vp, vp, vp, vp]
+    lib.fp8q_moe_combine.argtypes = [vp, i32, i64, i64, vp, vp, i64, i64, vp, i32, vp]
     for name in ("fp8q_quantize_act_1x128", "fp8q_quantize_w_128x128", "fp8q_gemm_blockscaled",
                  "fp8q_grouped_gemm_blockscaled", "fp8q_quantize_w_128x128_t", "fp8q_quantize_act_dual",
                  "fp8q_gemm_rowscaled", "fp8q_swiglu_quantize_act_1x128", "fp8q_quantize_per_tensor",
-                 "fp8q_quantize_act_w"):
+                 "fp8q_quantize_act_w", "fp8q_moe_dispatch", "fp8q_moe_combine"):
         getattr(lib, name).restype = i32
     lib.fp8q_status_string.argtypes = [i32]
     lib.fp8q_status_string.restype = ctypes.c_char_p
@@ -180,6 +183,57 @@ def fp8q_quantize_act_w(x: torch.Tensor, w: torch.Tensor, xq: torch.Tensor | Non
     _check(load_library().fp8q_quantize_act_w(_ptr(x), M, _ptr(w), G, N, K, _ptr(xq), _ptr(sa), _ptr(wq), _ptr(sb),
                                               _stream(stream)), "fp8q_quantize_act_w")
     return xq, sa, wq, sb
+
+
+def fp8q_moe_dispatch(topk_ids: torch.Tensor, xq: torch.Tensor, sa: torch.Tensor, e_begin: int, n_experts: int,
+                      capacity: int | None = None, stream=None):
+    """Expert-parallel dispatch of quantized tokens to the local experts [e_begin,
+    e_begin + n_experts): topk_ids int32 [T, k], xq uint8 [T, K], sa float32 [K/128, T] ->
+    (xq_sorted uint8 [capacity, K], sa_sorted float32 [K/128, capacity], offsets int32
+    [n_experts + 1], token_row int32 [T, k], row_token int32 [capacity]); capacity defaults
+    to T*k.  offsets feed fp8q_grouped_gemm_blockscaled with the sorted tensors."""
+    _need(topk_ids, torch.int32, "topk_ids")
+    if topk_ids.dim() != 2:
+        raise ValueError("topk_ids must be 2-D [T, k]")
+    T, k = topk_ids.shape
+    _need(xq, torch.uint8, "xq")
+    if xq.dim() != 2 or xq.shape[0] != T:
+        raise ValueError(f"xq must be [T={T}, K]")
+    K = xq.shape[1]
+    _need(sa, torch.float32, "sa", (K // 128, T))
+    cap = T * k if capacity is None else int(capacity)
+    dev = xq.device
+    xs = torch.empty((cap, K), dtype=torch.uint8, device=dev)
+    ss = torch.empty((K // 128, cap), dtype=torch.float32, device=dev)
+    offsets = torch.empty(n_experts + 1, dtype=torch.int32, device=dev)
+    token_row = torch.empty((T, k), dtype=torch.int32, device=dev)
+    row_token = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    _check(load_library().fp8q_moe_dispatch(_ptr(topk_ids), T, k, e_begin, n_experts, _ptr(xq), _ptr(sa), K, cap,
+                                            _ptr(xs), _ptr(ss), _ptr(offsets), _ptr(token_row), _ptr(row_token),
+                                            _stream(stream)), "fp8q_moe_dispatch")
+    return xs, ss, offsets, token_row, row_token[:cap]
+
+
+def fp8q_moe_combine(expert_out: torch.Tensor, token_row: torch.Tensor, topk_w: torch.Tensor,
+                     y: torch.Tensor | None = None, out_dtype=torch.bfloat16, stream=None):
+    """Expert-parallel combine: y[t] = sum over local slots of topk_w[t, s] * expert_out[token_row[t, s]]
+    (expert_out bf16 or float32 [capacity, N]; token_row int32 / topk_w float32 [T, k])."""
+    if expert_out.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("expert_out must be bfloat16 or float32")
+    _need(expert_out, expert_out.dtype, "expert_out")
+    _need(token_row, torch.int32, "token_row")
+    if token_row.dim() != 2 or expert_out.dim() != 2:
+        raise ValueError("token_row must be [T, k] and expert_out [capacity, N]")
+    T, k = token_row.shape
+    cap, N = expert_out.shape
+    _need(topk_w, torch.float32, "topk_w", (T, k))
+    if y is None:
+        y = torch.empty((T, N), dtype=out_dtype, device=expert_out.device)
+    _need(y, out_dtype, "y", (T, N))
+    _check(load_library().fp8q_moe_combine(_ptr(expert_out), _out_code(expert_out.dtype), cap, N, _ptr(token_row),
+                                           _ptr(topk_w), T, k, _ptr(y), _out_code(out_dtype), _stream(stream)),
+           "fp8q_moe_combine")
+    return y
 
 
 def _out_code(out_dtype) -> int:

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfp8q.so")
-SOURCES = ["quant.hip", "gemm.hip", "fp8q_abi.cpp"]
+SOURCES = ["quant.hip", "gemm.hip", "moe.hip", "fp8q_abi.cpp"]
 ARCH = "gfx950"
 
 

@@ -182,6 +182,43 @@ fp8q_status fp8q_quantize_per_tensor(const uint16_t *x_bf16, int64_t n, const fl
   return launched(fp8q::launch_quant_per_tensor(x_bf16, n, scale_in, q, stats, as_stream(stream)));
 }
 
+fp8q_status fp8q_moe_dispatch(const int32_t *topk_ids, int64_t T, int64_t k, int64_t e_begin, int64_t E,
+                              const uint8_t *xq, const float *sa, int64_t K, int64_t capacity, uint8_t *xq_sorted,
+                              float *sa_sorted, int32_t *offsets, int32_t *token_row, int32_t *row_token,
+                              void *stream) {
+  if (bad_dim(T) || k < 1 || k > 64 || bad_dim(K) || K % 128 != 0 || E < 1 || E > 1024 || e_begin < 0 ||
+      bad_dim(e_begin) || bad_dim(capacity))
+    return FP8Q_ERR_SHAPE;
+  if (too_many(T, k) || capacity < T * k || T * k >= kMaxDim || too_many(capacity, K) || too_many(T, K))
+    return FP8Q_ERR_SHAPE;
+  if (!offsets || (T > 0 && (!topk_ids || !token_row || !xq || !sa)) ||
+      (capacity > 0 && (!xq_sorted || !sa_sorted || !row_token)))
+    return FP8Q_ERR_NULL;
+  if (misaligned(topk_ids, 4) || misaligned(offsets, 4) || misaligned(token_row, 4) || misaligned(row_token, 4) ||
+      misaligned(xq) || misaligned(sa) || misaligned(xq_sorted) || misaligned(sa_sorted))
+    return FP8Q_ERR_ALIGN;
+  if (device_ok() != FP8Q_OK) return FP8Q_ERR_DEVICE;
+  return launched(fp8q::launch_moe_dispatch(topk_ids, T, k, e_begin, E, xq, sa, K, capacity, xq_sorted, sa_sorted,
+                                            offsets, token_row, row_token, as_stream(stream)));
+}
+
+fp8q_status fp8q_moe_combine(const void *expert_out, int32_t in_dtype, int64_t capacity, int64_t N,
+                             const int32_t *token_row, const float *topk_weights, int64_t T, int64_t k, void *y,
+                             int32_t out_dtype, void *stream) {
+  if ((in_dtype != FP8Q_OUT_BF16 && in_dtype != FP8Q_OUT_F32) || (out_dtype != FP8Q_OUT_BF16 && out_dtype != FP8Q_OUT_F32))
+    return FP8Q_ERR_DTYPE;
+  if (bad_dim(T) || k < 1 || k > 64 || bad_dim(N) || N % 8 != 0 || bad_dim(capacity) || too_many(T, k) ||
+      too_many(capacity, N) || too_many(T, N))
+    return FP8Q_ERR_SHAPE;
+  if (T == 0 || N == 0) return FP8Q_OK;
+  if (!token_row || !topk_weights || !y || (capacity > 0 && !expert_out)) return FP8Q_ERR_NULL;
+  if (misaligned(token_row, 4) || misaligned(topk_weights, 4) || misaligned(y) || misaligned(expert_out))
+    return FP8Q_ERR_ALIGN;
+  if (device_ok() != FP8Q_OK) return FP8Q_ERR_DEVICE;
+  return launched(fp8q::launch_moe_combine(expert_out, in_dtype == FP8Q_OUT_F32, capacity, N, token_row,
+                                           topk_weights, T, k, y, out_dtype == FP8Q_OUT_F32, as_stream(stream)));
+}
+
 const char *fp8q_status_string(fp8q_status status) {
   switch (status) {
     case FP8Q_OK: return "ok";

@@ -47,4 +47,16 @@ hipError_t launch_grouped_gemm(const uint8_t *xq, const float *sa, const uint8_t
                                const int32_t *offsets, int64_t G, int64_t M_tot, int64_t N, int64_t K,
                                void *c, bool out_f32, hipStream_t stream);
 
+// Expert-parallel dispatch on the GPU owning experts [e_begin, e_begin + E): route the
+// top-k ids [T][k] (offsets [E+1], token_row [T][k], row_token [cap]) and pack the routed
+// rows' codes xq [T][K] / scales sa [K/128][T] into xq_s [cap][K] / sa_s [K/128][cap].
+hipError_t launch_moe_dispatch(const int32_t *ids, int64_t T, int64_t k, int64_t e_begin, int64_t E,
+                               const uint8_t *xq, const float *sa, int64_t K, int64_t cap, uint8_t *xq_s,
+                               float *sa_s, int32_t *offsets, int32_t *token_row, int32_t *row_token,
+                               hipStream_t stream);
+
+// y[t] = sum over slots s with 0 <= token_row[t][s] < cap of w[t][s] * out[token_row[t][s]].
+hipError_t launch_moe_combine(const void *out, bool in_f32, int64_t cap, int64_t N, const int32_t *token_row,
+                              const float *w, int64_t T, int64_t k, void *y, bool out_f32, hipStream_t stream);
+
 }  // namespace fp8q

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define FP8Q_ABI_VERSION 6
+#define FP8Q_ABI_VERSION 7
 
 typedef int32_t fp8q_status;
 
@@ -241,6 +241,52 @@ fp8q_status fp8q_swiglu_quantize_act_1x128(const uint16_t *gu_bf16, int64_t M, i
  */
 fp8q_status fp8q_quantize_per_tensor(const uint16_t *x_bf16, int64_t n, const float *scale_in, uint8_t *q,
                                      uint32_t *stats, void *stream);
+
+/*
+ * Expert-parallel dispatch, one GPU's share: the GPU owning experts [e_begin, e_begin + E)
+ * lays out the tokens routed to them for the grouped GEMM.  Source: dlbhg.com page on
+ * DeepSeek-V3's training techniques, section 1.1 item 2 (8 of 256 routed experts per token),
+ * section 2.1 (64-way expert parallelism) and section 3.1 (all-to-all dispatch and combine);
+ * dtcms.com page, the DualPipe paragraph (dispatch and combine stages).  The all-to-all
+ * exchange itself is not part of this library; this is the work that sends (or, run on the
+ * received tokens, receives) E4M3 codes plus 1x128 tile scales, which is what the pages'
+ * FP8 scheme makes the payload (the quantizer is row-local, so quantizing before the
+ * exchange equals quantizing after it).
+ *   topk_ids   : DEVICE int32 [T][k], global expert ids (1 <= k <= 64; ids outside the local
+ *                range are skipped)
+ *   xq, sa     : the tokens' codes [T][K] and tile scales [K/128][T] (fp8q_quantize_act_1x128)
+ *   capacity   : rows of the outputs; must be >= T*k (every (token, slot) fits)
+ *   xq_sorted  : [capacity][K] out, sa_sorted : [K/128][capacity] out
+ *   offsets    : [E+1] out: expert e's rows are offsets[e] .. offsets[e+1]-1, experts in order,
+ *                tokens ascending within an expert (the grouped GEMM's offsets, with
+ *                M_tot = capacity; rows from offsets[E] on are not written)
+ *   token_row  : [T][k] out: the row of (t, s), or -1 if its expert is not local
+ *   row_token  : [capacity] out: the token of each row < offsets[E]
+ * Requires K % 128 == 0, 1 <= E <= 1024; with T == 0 only `offsets` is written (zeros).
+ * Two launches (routing in one workgroup, then the copy).  Errors: FP8Q_ERR_SHAPE, FP8Q_ERR_NULL, FP8Q_ERR_ALIGN (index arrays 4-byte, the
+ * rest 16-byte), FP8Q_ERR_DEVICE, FP8Q_ERR_LAUNCH.
+ */
+fp8q_status fp8q_moe_dispatch(const int32_t *topk_ids, int64_t T, int64_t k, int64_t e_begin, int64_t E,
+                              const uint8_t *xq, const float *sa, int64_t K, int64_t capacity, uint8_t *xq_sorted,
+                              float *sa_sorted, int32_t *offsets, int32_t *token_row, int32_t *row_token,
+                              void *stream);
+
+/*
+ * Expert-parallel combine, one GPU's share (sources as for fp8q_moe_dispatch):
+ *   y[t][n] = sum over slots s with 0 <= token_row[t][s] < capacity of
+ *             topk_weights[t][s] * expert_out[token_row[t][s]][n],
+ * FP32 fused multiply-adds in slot order, then y in out_dtype (BF16 round to nearest even,
+ * or FP32).  This is the local part of a token's output; the other GPUs' parts add the same
+ * way after the combine exchange.
+ *   expert_out : [capacity][N] in in_dtype (FP8Q_OUT_BF16 or FP8Q_OUT_F32), e.g. the
+ *                grouped GEMM's output on the dispatched rows
+ *   token_row, topk_weights : DEVICE [T][k] (fp8q_moe_dispatch; the gating weights)
+ *   y : [T][N] out.  Requires N % 8 == 0.  Errors: FP8Q_ERR_DTYPE, FP8Q_ERR_SHAPE,
+ *   FP8Q_ERR_NULL, FP8Q_ERR_ALIGN, FP8Q_ERR_DEVICE, FP8Q_ERR_LAUNCH.
+ */
+fp8q_status fp8q_moe_combine(const void *expert_out, int32_t in_dtype, int64_t capacity, int64_t N,
+                             const int32_t *token_row, const float *topk_weights, int64_t T, int64_t k, void *y,
+                             int32_t out_dtype, void *stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *fp8q_status_string(fp8q_status status);

@@ -184,3 +184,28 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros((4, 128), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fq.fp8q_quantize_act_1x128(x)
+
+
+def test_moe_entry_point_argument_checks(lib):
+    A = ALIGNED
+    E = header_enums()
+    d = lib.fp8q_moe_dispatch
+    #        ids T  k  e0 E   xq sa K    cap  xs ss off tr rt
+    assert d(A, 4, 8, 0, 32, A, A, 100, 32, A, A, A, A, A, None) == E["FP8Q_ERR_SHAPE"]    # K % 128
+    assert d(A, 4, 8, 0, 32, A, A, 128, 31, A, A, A, A, A, None) == E["FP8Q_ERR_SHAPE"]    # capacity < T*k
+    assert d(A, 4, 8, 0, 0, A, A, 128, 32, A, A, A, A, A, None) == E["FP8Q_ERR_SHAPE"]     # E < 1
+    assert d(A, 4, 8, 0, 2000, A, A, 128, 32, A, A, A, A, A, None) == E["FP8Q_ERR_SHAPE"]  # E > 1024
+    assert d(A, 4, 0, 0, 32, A, A, 128, 32, A, A, A, A, A, None) == E["FP8Q_ERR_SHAPE"]    # k < 1
+    assert d(0, 4, 8, 0, 32, A, A, 128, 32, A, A, A, A, A, None) == E["FP8Q_ERR_NULL"]
+    assert d(A, 4, 8, 0, 32, A, A, 128, 32, A, A, 0, A, A, None) == E["FP8Q_ERR_NULL"]
+    assert d(A + 2, 4, 8, 0, 32, A, A, 128, 32, A, A, A, A, A, None) == E["FP8Q_ERR_ALIGN"]
+    assert d(A, 4, 8, 0, 32, A, A + 4, 128, 32, A, A, A, A, A, None) == E["FP8Q_ERR_ALIGN"]
+    c = lib.fp8q_moe_combine
+    #        out dt cap N   tr wt T  k  y  dt
+    assert c(A, 2, 8, 64, A, A, 4, 2, A, 0, None) == E["FP8Q_ERR_DTYPE"]
+    assert c(A, 0, 8, 64, A, A, 4, 2, A, 3, None) == E["FP8Q_ERR_DTYPE"]
+    assert c(A, 0, 8, 60, A, A, 4, 2, A, 0, None) == E["FP8Q_ERR_SHAPE"]    # N % 8
+    assert c(A, 0, 8, 64, A, A, 4, 0, A, 0, None) == E["FP8Q_ERR_SHAPE"]    # k < 1
+    assert c(A, 0, 8, 64, A, A, 0, 2, 0, 0, None) == E["FP8Q_OK"]           # no tokens
+    assert c(A, 0, 8, 64, 0, A, 4, 2, A, 0, None) == E["FP8Q_ERR_NULL"]
+    assert c(A, 0, 8, 64, A, A, 4, 2, A + 2, 0, None) == E["FP8Q_ERR_ALIGN"]
