@@ -11,11 +11,15 @@ Steps 1 and 2 run as one launch (fp8q_quantize_act_w) unless --quant separate; e
 each quantizer is also timed in its own launches after the timed steps.
 Default workload: the dense projection X[4096x7168] x W[7168x7168]^T, BF16 out.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense|large|moe_up|moe_down|moe_ffn|train]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense|large|moe_up|moe_down|moe_ffn|moe_layer|train]
 
 The `moe_ffn` workload runs the expert FFN forward: activation and expert-weight
 quantization, the grouped up-projection, the fused SwiGLU + 1x128 quantizer, and the grouped
 down-projection; value = both GEMMs' FLOPs per step.
+The `moe_layer` workload runs the whole expert layer from the token side: both quantizers of
+X (token order) and W_up in one launch, the expert-parallel dispatch of the codes and scales
+to the 32 local experts' rows, the two grouped GEMMs with the fused SwiGLU quantizer and the
+W_down quantizer between them, and the gated combine back to the tokens.
 The `train` workload runs one training step of the dense layer instead: both-orientation
 quantization of X and dY, the transposing weight quantizer, and the three GEMMs (forward,
 dgrad through the W^T blocks, wgrad over token tiles); value = 3*2*M*N*K FLOPs per step.
@@ -58,6 +62,9 @@ WORKLOADS = {
                "X[8360x7168] -> up W[32][4096x7168] -> SwiGLU+quant -> down W[32][7168x2048], bf16 out",
     "train": "training step of the dense projection X[4096x7168], W[7168x7168]: forward Y = X W^T (bf16), "
              "dgrad dX = dY W (bf16), wgrad dW = dY^T X over the 4096 tokens (fp32)",
+    "moe_layer": "MoE expert layer from the token side, one GPU's share: 8192 tokens X[8192x7168] in token order, "
+                 "top-8 of 256 routing, 32 local experts: quantize X and W_up -> dispatch (8360 rows) -> up "
+                 "W[32][4096x7168] -> SwiGLU+quant -> down W[32][7168x2048] -> gated combine, bf16 out",
 }
 
 
@@ -227,6 +234,102 @@ def run_moe_ffn(args, torch, fq, dev):
     print(json.dumps(line), flush=True)
 
 
+def run_moe_layer(args, torch, fq, dev):
+    """The `moe_layer` workload (see the module docstring)."""
+    cfg = gen("moe_layer")
+    x_np, wu_np, wd_np, ids_np, gate_np = cfg["x"], cfg["w"], cfg["w_down"], cfg["topk_ids"], cfg["topk_w"]
+    T, K = x_np.shape
+    G, N1, _ = wu_np.shape
+    I = N1 // 2
+    # rows of this batch's dispatch: its routing is an input, so the buffers are sized to it
+    R = int(np.count_nonzero((ids_np >= cfg["e_begin"]) & (ids_np < cfg["e_begin"] + G)))
+    flops = 2.0 * R * N1 * K + 2.0 * R * K * I
+    x0 = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    wu0 = torch.from_numpy(wu_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    wd0 = torch.from_numpy(wd_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    ids = torch.from_numpy(ids_np).to(dev)
+    gate = torch.from_numpy(gate_np).to(dev)
+    per_set = 2 * (x0.numel() + wu0.numel() + wd0.numel()) * 2
+    nsets = min(8, args.sets or max(2, int(np.ceil(3 * 256e6 / per_set))))
+    u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
+    sets = []
+    for i in range(nsets):
+        sets.append({
+            "x": x0 if i == 0 else x0.clone(), "wu": wu0 if i == 0 else wu0.clone(), "wd": wd0 if i == 0 else wd0.clone(),
+            "xq": torch.empty((T, K), dtype=u8, device=dev), "sa": torch.empty((K // 128, T), dtype=f32, device=dev),
+            "wuq": torch.empty((G, N1, K), dtype=u8, device=dev), "sbu": torch.empty((G, N1 // 128, K // 128), dtype=f32, device=dev),
+            "wdq": torch.empty((G, K, I), dtype=u8, device=dev), "sbd": torch.empty((G, K // 128, I // 128), dtype=f32, device=dev),
+            "gu": torch.empty((R, N1), dtype=bf, device=dev),
+            "hq": torch.empty((R, I), dtype=u8, device=dev), "sh": torch.empty((I // 128, R), dtype=f32, device=dev),
+            "out": torch.empty((R, K), dtype=bf, device=dev), "y": torch.empty((T, K), dtype=bf, device=dev),
+        })
+    stream = torch.cuda.current_stream()
+    names = ["quant_act_w(X, W_up)", "dispatch", "grouped gemm up", "swiglu_quant(h)", "quant_w(W_down)",
+             "grouped gemm down", "combine"]
+    disp = {}
+
+    def step(s, ev=None):
+        def dispatch():
+            disp["r"] = fq.fp8q_moe_dispatch(ids, s["xq"], s["sa"], cfg["e_begin"], G, capacity=R, stream=stream)
+        calls = [
+            lambda: fq.fp8q_quantize_act_w(s["x"], s["wu"], xq=s["xq"], sa=s["sa"], wq=s["wuq"], sb=s["sbu"],
+                                           stream=stream),
+            dispatch,
+            lambda: fq.fp8q_grouped_gemm_blockscaled(disp["r"][0], disp["r"][1], s["wuq"], s["sbu"], disp["r"][2],
+                                                     out=s["gu"], stream=stream),
+            lambda: fq.fp8q_swiglu_quantize_act_1x128(s["gu"], xq=s["hq"], sa=s["sh"], stream=stream),
+            lambda: fq.fp8q_quantize_w_128x128(s["wd"], wq=s["wdq"], sb=s["sbd"], stream=stream),
+            lambda: fq.fp8q_grouped_gemm_blockscaled(s["hq"], s["sh"], s["wdq"], s["sbd"], disp["r"][2], out=s["out"],
+                                                     stream=stream),
+            lambda: fq.fp8q_moe_combine(s["out"], disp["r"][3], gate, y=s["y"], stream=stream),
+        ]
+        for i, c in enumerate(calls):
+            if ev is not None:
+                ev[i].record(stream)
+            c()
+        if ev is not None:
+            ev[len(calls)].record(stream)
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+    got_rows = int(disp["r"][2][-1].item())
+    if got_rows != R:
+        raise RuntimeError(f"dispatch produced {got_rows} rows, expected {R}")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % nsets], evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)])) * 1e3
+           for j, n in enumerate(names)}
+    gflops = {"grouped gemm up": 2.0 * R * N1 * K, "grouped gemm down": 2.0 * R * K * I}
+    tflops = {n: round(f / (per[n] * 1e-6) / 1e12, 1) for n, f in gflops.items()}
+    dom = max(gflops, key=lambda n: per[n])
+    disp_bytes = 2 * (R * K + 4 * R * (K // 128)) + 4 * T * 8 * 2   # codes + scales read and written, maps
+    comb_bytes = R * K * 2 + T * K * 2 + 8 * T * 8                  # expert outputs read, y written, maps
+    value = flops * args.steps / wall / 1e12
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic (seeded; shapes and distributions of the workload, no dataset)",
+        "config": {"workload": WORKLOADS["moe_layer"], "tokens": T, "rows": R, "hidden": K, "intermediate": I,
+                   "experts": G, "buffer_sets": nsets},
+        "pct_fp8_peak_step": round(value / PEAK_FP8_TFLOPS * 100, 2),
+        "kernels_us": {n: round(v, 2) for n, v in per.items()},
+        "gemm_tflops": tflops,
+        "dispatch_GBs": round(disp_bytes / (per["dispatch"] * 1e-6) / 1e9, 1),
+        "combine_GBs": round(comb_bytes / (per["combine"] * 1e-6) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": tflops[dom], "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops[dom] / PEAK_FP8_TFLOPS, 4), "traffic": None, "kernel": dom,
+                     "flop_per_launch": gflops[dom], "avg_launch_us": round(per[dom], 2)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def run_train(args, torch, fq, dev):
     """The `train` workload (see the module docstring)."""
     cfg = gen("train")
@@ -318,8 +421,8 @@ def main():
         sys.exit(1)
     fq.load_library()
     dev = torch.device("cuda:0")
-    if args.workload in ("train", "moe_ffn"):
-        (run_train if args.workload == "train" else run_moe_ffn)(args, torch, fq, dev)
+    if args.workload in ("train", "moe_ffn", "moe_layer"):
+        {"train": run_train, "moe_ffn": run_moe_ffn, "moe_layer": run_moe_layer}[args.workload](args, torch, fq, dev)
         return
 
     t_gen = time.perf_counter()

@@ -189,7 +189,7 @@ fp8q_status fp8q_moe_dispatch(const int32_t *topk_ids, int64_t T, int64_t k, int
   if (bad_dim(T) || k < 1 || k > 64 || bad_dim(K) || K % 128 != 0 || E < 1 || E > 1024 || e_begin < 0 ||
       bad_dim(e_begin) || bad_dim(capacity))
     return FP8Q_ERR_SHAPE;
-  if (too_many(T, k) || capacity < T * k || T * k >= kMaxDim || too_many(capacity, K) || too_many(T, K))
+  if (too_many(T, k) || T * k >= kMaxDim || too_many(capacity, K) || too_many(T, K))
     return FP8Q_ERR_SHAPE;
   if (!offsets || (T > 0 && (!topk_ids || !token_row || !xq || !sa)) ||
       (capacity > 0 && (!xq_sorted || !sa_sorted || !row_token)))

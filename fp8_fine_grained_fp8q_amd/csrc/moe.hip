@@ -24,6 +24,7 @@ namespace fp8q {
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kMaxLocalExperts = 1024;
+constexpr int kBatch = 16;  // 64-entry chunks whose id loads a wave issues together
 
 // Count of the set bits of mask below this lane.
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
@@ -36,9 +37,10 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 // waves' counts; a serial scan gives the offsets and each wave's first row per expert.
 // 3: each wave walks its entries again, 64 at a time: the lanes of one expert (found with a
 // ballot) take consecutive rows after that expert's running count, lower lanes first, so
-// rows follow the entry order, i.e. token order within an expert.
+// rows follow the entry order, i.e. token order within an expert.  A wave reads the ids of
+// kBatch chunks at once; its running counts live in a register for up to 64 experts.
 __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(const int32_t *__restrict__ ids, int64_t n,
-                                                                  int k, int64_t e_begin, int E,
+                                                                  int k, int64_t e_begin, int E, int64_t cap,
                                                                   int32_t *__restrict__ offsets,
                                                                   int32_t *__restrict__ token_row,
                                                                   int32_t *__restrict__ row_token) {
@@ -54,9 +56,14 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(const int32_t 
   };
   for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) cnt[i] = 0;
   __syncthreads();
-  for (int64_t c = lo; c < hi; c += 64) {
-    const int e = local_expert(c + lane);
-    if (e >= 0) atomicAdd(&cnt[wave * E + e], 1);
+  // The id loads of kBatch chunks are issued together (one wave walks its range serially).
+  for (int64_t c0 = lo; c0 < hi; c0 += 64 * kBatch) {
+    int eb[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) eb[b] = local_expert(c0 + 64 * b + lane);
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b)
+      if (eb[b] >= 0) atomicAdd(&cnt[wave * E + eb[b]], 1);
   }
   __syncthreads();
   for (int e = tid; e < E; e += kRouteThreads) {
@@ -85,22 +92,40 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(const int32_t 
     }
   }
   __syncthreads();
-  for (int64_t c = lo; c < hi; c += 64) {
-    const int64_t idx = c + lane;
-    const int e = local_expert(idx);
-    int row = -1;
-    uint64_t pending = __ballot(e >= 0);
-    while (pending != 0) {
-      const int leader = __ffsll(static_cast<long long>(pending)) - 1;
-      const int ee = __shfl(e, leader);
-      const uint64_t m = __ballot(e == ee);
-      const int r0 = cnt[wave * E + ee];
-      if (e == ee) row = r0 + lanes_below(m);
-      if (lane == leader) cnt[wave * E + ee] = r0 + __popcll(m);
-      pending &= ~m;
+  // Up to 64 local experts: lane e of each wave keeps the wave's running row of expert e in
+  // a register, so ranking a chunk needs no LDS traffic (readlane of uniform lanes only).
+  const bool in_regs = E <= 64;
+  int run = in_regs && lane < E ? cnt[wave * E + lane] : 0;
+  for (int64_t c0 = lo; c0 < hi; c0 += 64 * kBatch) {
+    int eb[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) eb[b] = local_expert(c0 + 64 * b + lane);
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {  // chunks in entry order
+      const int64_t idx = c0 + 64 * b + lane;
+      const int e = eb[b];
+      int row = -1;
+      uint64_t pending = __ballot(e >= 0);
+      while (pending != 0) {
+        const int leader = __ffsll(static_cast<long long>(pending)) - 1;
+        const int ee = __builtin_amdgcn_readlane(e, leader);
+        const uint64_t m = __ballot(e == ee);
+        if (in_regs) {
+          const int r0 = __builtin_amdgcn_readlane(run, ee);
+          if (e == ee) row = r0 + lanes_below(m);
+          if (lane == ee) run = r0 + __popcll(m);
+        } else {
+          const int r0 = cnt[wave * E + ee];
+          if (e == ee) row = r0 + lanes_below(m);
+          if (lane == leader) cnt[wave * E + ee] = r0 + __popcll(m);
+        }
+        pending &= ~m;
+      }
+      // rows past the capacity are dropped (their slots read as not local); offsets still
+      // count them, so the caller can see that the capacity was too small
+      if (idx < hi) token_row[idx] = row < cap ? row : -1;
+      if (row >= 0 && row < cap) row_token[row] = static_cast<int32_t>(idx / k);
     }
-    if (idx < hi) token_row[idx] = row;
-    if (row >= 0) row_token[row] = static_cast<int32_t>(idx / k);
   }
 }
 
@@ -112,7 +137,7 @@ __global__ __launch_bounds__(256) void moe_pack_kernel(const uint8_t *__restrict
                                                        uint8_t *__restrict__ xq_s, float *__restrict__ sa_s) {
   const int lane = threadIdx.x & 63;
   const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (r >= offsets[E]) return;
+  if (r >= offsets[E] || r >= cap) return;
   const int64_t t = row_token[r];
   const uint4 *src = reinterpret_cast<const uint4 *>(xq + t * K);
   uint4 *dst = reinterpret_cast<uint4 *>(xq_s + r * K);
@@ -180,7 +205,7 @@ hipError_t launch_moe_dispatch(const int32_t *ids, int64_t T, int64_t k, int64_t
                                hipStream_t stream) {
   if (E < 1 || E > kMaxLocalExperts || (cap + 3) / 4 > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, stream, ids, T * k, static_cast<int>(k),
-                     e_begin, static_cast<int>(E), offsets, token_row, row_token);
+                     e_begin, static_cast<int>(E), cap, offsets, token_row, row_token);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || cap == 0) return e;
   hipLaunchKernelGGL(moe_pack_kernel, dim3(static_cast<uint32_t>((cap + 3) / 4)), dim3(256), 0, stream, xq, sa, T,

@@ -255,11 +255,13 @@ fp8q_status fp8q_quantize_per_tensor(const uint16_t *x_bf16, int64_t n, const fl
  *   topk_ids   : DEVICE int32 [T][k], global expert ids (1 <= k <= 64; ids outside the local
  *                range are skipped)
  *   xq, sa     : the tokens' codes [T][K] and tile scales [K/128][T] (fp8q_quantize_act_1x128)
- *   capacity   : rows of the outputs; must be >= T*k (every (token, slot) fits)
+ *   capacity   : rows of the outputs.  T*k always suffices; with fewer, the rows from
+ *                `capacity` on are dropped (their slots get token_row -1) while offsets
+ *                still count them, so offsets[E] > capacity tells the caller it was short
  *   xq_sorted  : [capacity][K] out, sa_sorted : [K/128][capacity] out
  *   offsets    : [E+1] out: expert e's rows are offsets[e] .. offsets[e+1]-1, experts in order,
  *                tokens ascending within an expert (the grouped GEMM's offsets, with
- *                M_tot = capacity; rows from offsets[E] on are not written)
+ *                M_tot = capacity, which clamps them; rows from offsets[E] on are not written)
  *   token_row  : [T][k] out: the row of (t, s), or -1 if its expert is not local
  *   row_token  : [capacity] out: the token of each row < offsets[E]
  * Requires K % 128 == 0, 1 <= E <= 1024; with T == 0 only `offsets` is written (zeros).

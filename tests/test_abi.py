@@ -192,7 +192,7 @@ def test_moe_entry_point_argument_checks(lib):
     d = lib.fp8q_moe_dispatch
     #        ids T  k  e0 E   xq sa K    cap  xs ss off tr rt
     assert d(A, 4, 8, 0, 32, A, A, 100, 32, A, A, A, A, A, None) == E["FP8Q_ERR_SHAPE"]    # K % 128
-    assert d(A, 4, 8, 0, 32, A, A, 128, 31, A, A, A, A, A, None) == E["FP8Q_ERR_SHAPE"]    # capacity < T*k
+    assert d(A, 4, 8, 0, 32, A, A, 128, -1, A, A, A, A, A, None) == E["FP8Q_ERR_SHAPE"]    # capacity < 0
     assert d(A, 4, 8, 0, 0, A, A, 128, 32, A, A, A, A, A, None) == E["FP8Q_ERR_SHAPE"]     # E < 1
     assert d(A, 4, 8, 0, 2000, A, A, 128, 32, A, A, A, A, A, None) == E["FP8Q_ERR_SHAPE"]  # E > 1024
     assert d(A, 4, 0, 0, 32, A, A, 128, 32, A, A, A, A, A, None) == E["FP8Q_ERR_SHAPE"]    # k < 1

@@ -67,6 +67,25 @@ def test_dispatch_degenerate():
     assert host(off).tolist() == [0, 0, 0, 0, 0]
 
 
+def test_dispatch_short_capacity():
+    """A capacity below the routed count: the first `capacity` rows are as with room for
+    all, the later ones are dropped (their slots read -1) and offsets still count them."""
+    rng = np.random.default_rng(8)
+    T, k, E, K = 200, 4, 16, 256
+    x = wl.bf16_bits(rng.standard_normal((T, K), dtype=np.float32))
+    ids = np.stack([rng.choice(32, k, replace=False) for _ in range(T)]).astype(np.int32)
+    roff, rrt, rtr = om.dispatch(ids, 0, E)
+    cap = int(roff[-1]) - 37
+    xq, sa = fq.fp8q_quantize_act_1x128(dev_bf16(x))
+    xs, ss, off, tr, rt = fq.fp8q_moe_dispatch(dev(ids), xq, sa, 0, E, capacity=cap)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(off), roff)
+    assert np.array_equal(host(tr), np.where(rtr < cap, rtr, -1))
+    assert np.array_equal(host(rt), rrt[:cap])
+    pq, psa = om.pack(*oq.quantize_act_1x128(x), rrt[:cap])
+    assert np.array_equal(host(xs), pq) and np.array_equal(host(ss).view(np.uint32), psa.view(np.uint32))
+
+
 def combine_check(out_d, token_row, w, out_dtype):
     """GPU combine of the expert outputs out_d (bf16 or float32 [capacity, N], CUDA) against
     the oracle's, within the bound of FP32 accumulation in slot order plus the output
