@@ -24,7 +24,7 @@ namespace fp8q {
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kMaxLocalExperts = 1024;
-constexpr int kBatch = 16;  // 64-entry chunks whose id loads a wave issues together
+constexpr int64_t kChunk = 1024;  // (token, slot) entries per routing workgroup; >= kMaxLocalExperts
 
 // Count of the set bits of mask below this lane.
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
@@ -32,100 +32,181 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u)));
 }
 
-// One workgroup.  Wave w owns the (token, slot) entries [w*per, (w+1)*per) of ids[T*k] in
-// order.  1: per-wave, per-expert counts (LDS atomics).  2: one thread per expert sums the
-// waves' counts; a serial scan gives the offsets and each wave's first row per expert.
-// 3: each wave walks its entries again, 64 at a time: the lanes of one expert (found with a
-// ballot) take consecutive rows after that expert's running count, lower lanes first, so
-// rows follow the entry order, i.e. token order within an expert.  A wave reads the ids of
-// kBatch chunks at once; its running counts live in a register for up to 64 experts.
-__global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(const int32_t *__restrict__ ids, int64_t n,
-                                                                  int k, int64_t e_begin, int E, int64_t cap,
-                                                                  int32_t *__restrict__ offsets,
-                                                                  int32_t *__restrict__ token_row,
-                                                                  int32_t *__restrict__ row_token) {
-  __shared__ int32_t cnt[kRouteWaves * kMaxLocalExperts];  // counts, then running rows
-  __shared__ int32_t tot[kMaxLocalExperts];
+// The routing splits the n = T*k entries into C = max(1, floor(n / kChunk)) chunks of
+// kChunk entries in order, the last one taking the remainder (so every chunk but a lone one
+// holds at least kChunk >= E entries).  Entry range of chunk c:
+__device__ __forceinline__ void chunk_range(int64_t c, int64_t C, int64_t n, int64_t &lo, int64_t &hi) {
+  lo = c * kChunk;
+  hi = c == C - 1 ? n : lo + kChunk;
+}
+
+__device__ __forceinline__ int local_expert(const int32_t *__restrict__ ids, int64_t idx, int64_t hi,
+                                            int64_t e_begin, int E) {
+  if (idx >= hi) return -1;
+  const int64_t g = static_cast<int64_t>(ids[idx]) - e_begin;
+  return g >= 0 && g < E ? static_cast<int>(g) : -1;
+}
+
+// Exclusive prefix sum of v over the kRouteThreads threads in thread order; *total gets the
+// sum.  Every thread of the workgroup calls it; ws is kRouteWaves ints of LDS.
+__device__ __forceinline__ int block_exclusive_scan(int v, int *ws, int *total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(inc, d);
+    if (lane >= d) inc += u;
+  }
+  if (lane == 63) ws[wave] = inc;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kRouteWaves; ++w) {
+    const int t = ws[w];
+    before += w < wave ? t : 0;
+    all += t;
+  }
+  __syncthreads();  // ws may be reused after this
+  *total = all;
+  return before + inc - v;
+}
+
+// 1 (C > 1 only): each workgroup counts its chunk's entries per local expert and leaves the
+// counts in the first E entries of its own range of token_row, which the ranking pass
+// overwrites later (only this chunk's workgroups ever touch that range).
+__global__ __launch_bounds__(kRouteThreads) void moe_count_kernel(const int32_t *__restrict__ ids, int64_t n,
+                                                                  int64_t C, int64_t e_begin, int E,
+                                                                  int32_t *__restrict__ token_row) {
+  __shared__ int32_t hist[kMaxLocalExperts];
+  int64_t lo, hi;
+  chunk_range(blockIdx.x, C, n, lo, hi);
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) hist[e] = 0;
+  __syncthreads();
+  for (int64_t i = lo + threadIdx.x; i < hi; i += kRouteThreads) {
+    const int e = local_expert(ids, i, hi, e_begin, E);
+    if (e >= 0) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) token_row[lo + e] = hist[e];
+}
+
+// 2 (C > 1 only), one workgroup: offsets[e] = rows of the experts before e, and in place of
+// chunk c's count of expert e, that chunk's first row of expert e (offsets[e] plus the counts
+// of the earlier chunks).  Thread (g, e) = (tid / E, tid % E) walks a contiguous run of
+// chunks for expert e; the runs' sums are scanned per expert, the experts' totals over the
+// workgroup.
+__global__ __launch_bounds__(kRouteThreads) void moe_scan_kernel(int64_t n, int64_t C, int E,
+                                                                 int32_t *__restrict__ offsets,
+                                                                 int32_t *__restrict__ token_row) {
+  __shared__ int32_t part[kRouteThreads];
+  __shared__ int32_t first[kMaxLocalExperts];
+  __shared__ int32_t ws[kRouteWaves];
+  const int tid = threadIdx.x;
+  const int G = kRouteThreads / E;
+  const int64_t per = (C + G - 1) / G;
+  const int g = tid / E, e = tid % E;
+  const int64_t c_lo = g < G ? g * per : C, c_hi = c_lo + per < C ? c_lo + per : C;
+  int s = 0;
+  for (int64_t c = c_lo; c < c_hi; ++c) s += token_row[c * kChunk + e];
+  if (g < G) part[tid] = s;
+  __syncthreads();
+  int tot = 0;
+  if (tid < E) {
+    for (int j = 0; j < G; ++j) {  // runs before g, per expert
+      const int p = part[j * E + tid];
+      part[j * E + tid] = tot;
+      tot += p;
+    }
+  }
+  int all;
+  const int ex = block_exclusive_scan(tid < E ? tot : 0, ws, &all);
+  if (tid < E) {
+    offsets[tid] = ex;
+    first[tid] = ex;
+  }
+  if (tid == 0) offsets[E] = all;
+  __syncthreads();
+  int base = g < G ? first[e] + part[tid] : 0;
+  for (int64_t c = c_lo; c < c_hi; ++c) {
+    const int v = token_row[c * kChunk + e];
+    token_row[c * kChunk + e] = base;
+    base += v;
+  }
+}
+
+// 3: each workgroup ranks its chunk, 1024 entries per round, one per thread.  Within a wave
+// the lanes of one expert are found without a loop: the ballots of the expert index's bits
+// (and of "local") intersect to the set of lanes with this lane's expert.  A lane's row is
+// the chunk's running row of its expert, plus that expert's entries in the earlier waves of
+// the round, plus those in lower lanes, so rows follow entry order, i.e. token order within
+// an expert.  With a lone chunk (C == 1) the workgroup counts and scans by itself and writes
+// the offsets.
+__global__ __launch_bounds__(kRouteThreads) void moe_rank_kernel(const int32_t *__restrict__ ids, int64_t n,
+                                                                 int64_t C, int k, int64_t e_begin, int E,
+                                                                 int64_t cap, int32_t *__restrict__ offsets,
+                                                                 int32_t *__restrict__ token_row,
+                                                                 int32_t *__restrict__ row_token) {
+  __shared__ int32_t run[kMaxLocalExperts];                  // the chunk's next row, per expert
+  __shared__ int32_t wcnt[kRouteWaves * kMaxLocalExperts];   // a round's count per wave and expert
+  __shared__ int32_t ws[kRouteWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t per = ((n + kRouteWaves - 1) / kRouteWaves + 63) / 64 * 64;
-  const int64_t lo = wave * per, hi = lo + per < n ? lo + per : n;
-  auto local_expert = [&](int64_t idx) -> int {
-    if (idx >= hi) return -1;
-    const int64_t g = static_cast<int64_t>(ids[idx]) - e_begin;
-    return g >= 0 && g < E ? static_cast<int>(g) : -1;
-  };
-  for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) cnt[i] = 0;
-  __syncthreads();
-  // The id loads of kBatch chunks are issued together (one wave walks its range serially).
-  for (int64_t c0 = lo; c0 < hi; c0 += 64 * kBatch) {
-    int eb[kBatch];
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) eb[b] = local_expert(c0 + 64 * b + lane);
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b)
-      if (eb[b] >= 0) atomicAdd(&cnt[wave * E + eb[b]], 1);
-  }
-  __syncthreads();
-  for (int e = tid; e < E; e += kRouteThreads) {
-    int s = 0;
-    for (int w = 0; w < kRouteWaves; ++w) s += cnt[w * E + e];
-    tot[e] = s;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int e = 0; e < E; ++e) {
-      offsets[e] = run;
-      const int t = tot[e];
-      tot[e] = run;
-      run += t;
+  int64_t lo, hi;
+  chunk_range(blockIdx.x, C, n, lo, hi);
+  for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) wcnt[i] = 0;
+  if (C > 1) {
+    for (int e = tid; e < E; e += kRouteThreads) run[e] = token_row[lo + e];
+  } else {
+    for (int e = tid; e < E; e += kRouteThreads) run[e] = 0;
+    __syncthreads();
+    for (int64_t i = lo + tid; i < hi; i += kRouteThreads) {
+      const int e = local_expert(ids, i, hi, e_begin, E);
+      if (e >= 0) atomicAdd(&run[e], 1);
     }
-    offsets[E] = run;
-  }
-  __syncthreads();
-  for (int e = tid; e < E; e += kRouteThreads) {  // each wave's first row of expert e
-    int base = tot[e];
-    for (int w = 0; w < kRouteWaves; ++w) {
-      const int c = cnt[w * E + e];
-      cnt[w * E + e] = base;
-      base += c;
+    __syncthreads();
+    int all;
+    const int cnt = tid < E ? run[tid] : 0;
+    const int ex = block_exclusive_scan(cnt, ws, &all);
+    if (tid < E) {
+      run[tid] = ex;
+      offsets[tid] = ex;
     }
+    if (tid == 0) offsets[E] = all;
   }
-  __syncthreads();
-  // Up to 64 local experts: lane e of each wave keeps the wave's running row of expert e in
-  // a register, so ranking a chunk needs no LDS traffic (readlane of uniform lanes only).
-  const bool in_regs = E <= 64;
-  int run = in_regs && lane < E ? cnt[wave * E + lane] : 0;
-  for (int64_t c0 = lo; c0 < hi; c0 += 64 * kBatch) {
-    int eb[kBatch];
+  __syncthreads();  // the counts in token_row are read before this chunk's rows overwrite them
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  for (int64_t r0 = lo; r0 < hi; r0 += kRouteThreads) {
+    const int64_t idx = r0 + tid;
+    const int e = local_expert(ids, idx, hi, e_begin, E);
+    uint64_t m = __ballot(e >= 0);
+    for (int b = 0; b < nbits; ++b) {
+      const uint64_t bit = __ballot(e >= 0 && ((e >> b) & 1));
+      m &= ((e >> b) & 1) ? bit : ~bit;
+    }
+    const bool leader = e >= 0 && lanes_below(m) == 0;
+    if (leader) wcnt[wave * E + e] = __popcll(m);
+    __syncthreads();
+    int row = -1, last_wave = -1, round_total = 0;
+    if (e >= 0) {
+      int before = 0;
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) eb[b] = local_expert(c0 + 64 * b + lane);
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) {  // chunks in entry order
-      const int64_t idx = c0 + 64 * b + lane;
-      const int e = eb[b];
-      int row = -1;
-      uint64_t pending = __ballot(e >= 0);
-      while (pending != 0) {
-        const int leader = __ffsll(static_cast<long long>(pending)) - 1;
-        const int ee = __builtin_amdgcn_readlane(e, leader);
-        const uint64_t m = __ballot(e == ee);
-        if (in_regs) {
-          const int r0 = __builtin_amdgcn_readlane(run, ee);
-          if (e == ee) row = r0 + lanes_below(m);
-          if (lane == ee) run = r0 + __popcll(m);
-        } else {
-          const int r0 = cnt[wave * E + ee];
-          if (e == ee) row = r0 + lanes_below(m);
-          if (lane == leader) cnt[wave * E + ee] = r0 + __popcll(m);
-        }
-        pending &= ~m;
+      for (int w = 0; w < kRouteWaves; ++w) {
+        const int t = wcnt[w * E + e];
+        before += w < wave ? t : 0;
+        round_total += t;
+        last_wave = t > 0 ? w : last_wave;
       }
-      // rows past the capacity are dropped (their slots read as not local); offsets still
-      // count them, so the caller can see that the capacity was too small
-      if (idx < hi) token_row[idx] = row < cap ? row : -1;
-      if (row >= 0 && row < cap) row_token[row] = static_cast<int32_t>(idx / k);
+      row = run[e] + before + lanes_below(m);
     }
+    __syncthreads();  // every lane has read run[] and wcnt[]
+    if (leader) {
+      wcnt[wave * E + e] = 0;
+      if (last_wave == wave) run[e] += round_total;
+    }
+    // rows past the capacity are dropped (their slots read as not local); offsets still count
+    // them, so the caller can see that the capacity was too small
+    if (idx < hi) token_row[idx] = row < cap ? row : -1;
+    if (row >= 0 && row < cap) row_token[row] = static_cast<int32_t>(idx / k);
+    __syncthreads();
   }
 }
 
@@ -204,8 +285,16 @@ hipError_t launch_moe_dispatch(const int32_t *ids, int64_t T, int64_t k, int64_t
                                float *sa_s, int32_t *offsets, int32_t *token_row, int32_t *row_token,
                                hipStream_t stream) {
   if (E < 1 || E > kMaxLocalExperts || (cap + 3) / 4 > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, stream, ids, T * k, static_cast<int>(k),
-                     e_begin, static_cast<int>(E), cap, offsets, token_row, row_token);
+  const int64_t n = T * k, C = n / kChunk > 1 ? n / kChunk : 1;
+  if (C > 0x7fffffff) return hipErrorInvalidValue;
+  const int kk = static_cast<int>(k), EE = static_cast<int>(E);
+  if (C > 1) {
+    hipLaunchKernelGGL(moe_count_kernel, dim3(static_cast<uint32_t>(C)), dim3(kRouteThreads), 0, stream, ids, n, C,
+                       e_begin, EE, token_row);
+    hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(kRouteThreads), 0, stream, n, C, EE, offsets, token_row);
+  }
+  hipLaunchKernelGGL(moe_rank_kernel, dim3(static_cast<uint32_t>(C)), dim3(kRouteThreads), 0, stream, ids, n, C, kk,
+                     e_begin, EE, cap, offsets, token_row, row_token);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || cap == 0) return e;
   hipLaunchKernelGGL(moe_pack_kernel, dim3(static_cast<uint32_t>((cap + 3) / 4)), dim3(256), 0, stream, xq, sa, T,

@@ -265,7 +265,8 @@ fp8q_status fp8q_quantize_per_tensor(const uint16_t *x_bf16, int64_t n, const fl
  *   token_row  : [T][k] out: the row of (t, s), or -1 if its expert is not local
  *   row_token  : [capacity] out: the token of each row < offsets[E]
  * Requires K % 128 == 0, 1 <= E <= 1024; with T == 0 only `offsets` is written (zeros).
- * Two launches (routing in one workgroup, then the copy).  Errors: FP8Q_ERR_SHAPE, FP8Q_ERR_NULL, FP8Q_ERR_ALIGN (index arrays 4-byte, the
+ * Up to four launches (count, scan and rank over chunks of 1024 entries, then the copy);
+ * token_row serves as the count pass's scratch.  Errors: FP8Q_ERR_SHAPE, FP8Q_ERR_NULL, FP8Q_ERR_ALIGN (index arrays 4-byte, the
  * rest 16-byte), FP8Q_ERR_DEVICE, FP8Q_ERR_LAUNCH.
  */
 fp8q_status fp8q_moe_dispatch(const int32_t *topk_ids, int64_t T, int64_t k, int64_t e_begin, int64_t E,

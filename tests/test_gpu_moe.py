@@ -43,12 +43,17 @@ def assert_dispatch_equal(got, ref):
     assert np.array_equal(ss[:, :R].view(np.uint32), psa.view(np.uint32)), "packed scales"
 
 
-@pytest.mark.parametrize("T,k,E,e_begin,K", [(300, 8, 20, 16, 384), (77, 1, 5, 0, 128), (129, 3, 64, 0, 256),
-                                             (64, 6, 1, 9, 128)])
-def test_dispatch_random(T, k, E, e_begin, K):
+# The routing works in chunks of 1024 (token, slot) entries, the last taking the remainder
+# (one chunk below 2048 entries): lone chunks, two chunks with a two-round tail, many chunks
+# per scan thread (C > 1024 / E), E = 1024 (one scan thread per expert), E = 1.
+@pytest.mark.parametrize("T,k,E,e_begin,K,id_range", [(300, 8, 20, 16, 384, 64), (77, 1, 5, 0, 128, 64),
+                                                      (129, 3, 64, 0, 256, 64), (64, 6, 1, 9, 128, 64),
+                                                      (4100, 8, 512, 100, 128, 1024), (300, 8, 1024, 0, 128, 1500),
+                                                      (2048, 1, 1, 3, 128, 8)])
+def test_dispatch_random(T, k, E, e_begin, K, id_range):
     rng = np.random.default_rng(T * 31 + k * 7 + E)
     x = wl.bf16_bits(rng.standard_normal((T, K), dtype=np.float32) * np.float32(4.0))
-    ids = rng.integers(0, 64, size=(T, k)).astype(np.int32)  # duplicates and non-local ids included
+    ids = rng.integers(0, id_range, size=(T, k)).astype(np.int32)  # duplicates and non-local ids included
     got, ref = dispatch_both(x, ids, e_begin, E)
     assert_dispatch_equal(got, ref)
 
