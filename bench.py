@@ -27,8 +27,17 @@ dgrad through the W^T blocks, wgrad over token tiles); value = 3*2*M*N*K FLOPs p
 Prints ONE JSON line.  `value` = 2*M*N*K*steps / (timed wall time of the steps), i.e. GEMM
 TFLOP/s including both online quantizers.  Inputs are resident in HBM before timing.  To
 keep the 256 MB Infinity Cache from serving repeated steps, steps rotate over several
-buffer sets (together larger than the cache).  Per-kernel durations come from HIP events
-recorded on the stream the kernels run on.  `roofline` describes the dominant kernel (the
+buffer sets (together larger than the cache).
+
+Timing phases: (1) warm-up: the W untimed steps, continued back to back until at least
+--settle-ms of them have run, because the GPU's clocks take tens of milliseconds of
+sustained load to settle (per-step time falls by about 15 % over the first ~50 ms of
+back-to-back steps and then holds); (2) the timed region: exactly K steps launched back to
+back, bracketed by a device synchronize and HIP events on the kernels' stream, nothing
+recorded between the kernels; (3) the kernel-timing pass: K more steps, identical but with
+a HIP event recorded on the kernels' stream between consecutive launches, which gives each
+kernel's average launch duration (each event adds a marker between two kernels, which is
+why the timed region records none).  `roofline` describes the dominant kernel (the
 GEMM): algorithmic FLOPs per launch / its average duration, against the 5.0 PFLOP/s dense
 FP8 peak.  `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 """
@@ -73,11 +82,17 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="continue the untimed warm-up steps until this many ms of them have run")
     ap.add_argument("--workload", default="dense", choices=sorted(WORKLOADS))
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0: enough to exceed the 256 MB cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quant", choices=("fused", "separate"), default="fused",
                     help="quantize X and W in one launch (fp8q_quantize_act_w) or in two")
+    ap.add_argument("--vendor-context", action="store_true",
+                    help="also time hipBLASLt's FP8 GEMM (torch._scaled_mm, per-tensor and row-wise scales, "
+                         "no per-128-K promotion) on the same shape; reported as vendor_context, not part of "
+                         "the step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy per step (untimed) for counter calibration")
     return ap.parse_args()
@@ -104,6 +119,80 @@ def measured_traffic(workload: str):
     if t.get("gemm_source_sha256_16") != source_hash():
         return None
     return t.get("workloads", {}).get(workload, {}).get("bytes_per_launch")
+
+
+def run_steps(torch, args, step, n_calls):
+    """The three timing phases (module docstring) around `step(i, ev)`, which launches step
+    i's kernels on the current stream, recording ev[j] before its j-th launch and ev[n_calls]
+    after the last one when ev is given.  Returns (wall seconds of the K timed steps, device
+    seconds between the timed region's bracketing events, mean microseconds per launch from
+    the kernel-timing pass, warm-up steps run)."""
+    stream = torch.cuda.current_stream()
+    n = 0
+    t0 = time.perf_counter()
+    while n < args.warmup or (time.perf_counter() - t0) * 1e3 < args.settle_ms:
+        step(n, None)
+        n += 1
+        if n % 10 == 0:  # keeps the host at most 10 steps ahead of the GPU
+            torch.cuda.synchronize()
+    K_steps = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(K_steps):
+        step(n + i, None)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_dev = e0.elapsed_time(e1) * 1e-3
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_calls + 1)] for _ in range(K_steps)]
+    for i in range(K_steps):
+        step(n + K_steps + i, evs[i])
+    torch.cuda.synchronize()
+    per = [float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K_steps)])) * 1e3
+           for j in range(n_calls)]
+    return wall, t_dev, per, n
+
+
+def timing_fields(args, wall, t_dev, warm):
+    """The JSON fields that describe the timing phases."""
+    return {"warmup_steps_run": warm, "settle_ms": args.settle_ms,
+            "device_ms_per_step": round(t_dev / args.steps * 1e3, 4),
+            "kernel_timing": "HIP events between launches in a second pass of K identical steps"}
+
+
+def vendor_context(torch, M, N, K, steps):
+    """hipBLASLt's FP8 GEMM on the same shape through torch._scaled_mm (E4M3 operands, BF16
+    out; one scale per tensor, then one per row and column): mean microseconds of `steps`
+    back-to-back launches after 20 untimed ones.  Context only: neither form applies
+    per-128-K block scales."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(0)
+    a = (torch.randn(M, K, device=dev, generator=g) * 50).to(torch.float8_e4m3fn)
+    b = (torch.randn(N, K, device=dev, generator=g) * 50).to(torch.float8_e4m3fn)
+    one = torch.ones((), device=dev)
+    sa, sb = torch.ones(M, 1, device=dev), torch.ones(1, N, device=dev)
+    out = {}
+    for kind, (x, y) in (("per_tensor", (one, one)), ("rowwise", (sa, sb))):
+        try:
+            def run():
+                return torch._scaled_mm(a, b.t(), scale_a=x, scale_b=y, out_dtype=torch.bfloat16)
+            for _ in range(20):
+                run()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(steps):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / steps * 1e3
+            out[f"hipblaslt_scaled_mm_{kind}_us"] = round(us, 1)
+            out[f"hipblaslt_scaled_mm_{kind}_tflops"] = round(2.0 * M * N * K / us / 1e6, 1)
+        except Exception as ex:  # pragma: no cover - depends on the installed torch
+            out[f"hipblaslt_scaled_mm_{kind}"] = f"unavailable: {type(ex).__name__}"
+    return out
 
 
 def cpu_baseline(cfg, flops_step):
@@ -181,7 +270,8 @@ def run_moe_ffn(args, torch, fq, dev):
     names = ["quant_act(X)", "quant_w(W_up)", "grouped gemm up", "swiglu_quant(h)", "quant_w(W_down)",
              "grouped gemm down"]
 
-    def step(s, ev=None):
+    def step(i, ev=None):
+        s = sets[i % nsets]
         calls = [
             lambda: fq.fp8q_quantize_act_1x128(s["x"], xq=s["xq"], sa=s["sa"], stream=stream),
             lambda: fq.fp8q_quantize_w_128x128(s["wu"], wq=s["wuq"], sb=s["sbu"], stream=stream),
@@ -199,17 +289,8 @@ def run_moe_ffn(args, torch, fq, dev):
         if ev is not None:
             ev[len(calls)].record(stream)
 
-    for i in range(args.warmup):
-        step(sets[i % nsets])
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(sets[i % nsets], evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)])) * 1e3
-           for j, n in enumerate(names)}
+    wall, t_dev, per_l, warm = run_steps(torch, args, step, len(names))
+    per = dict(zip(names, per_l))
     gflops = {"grouped gemm up": 2.0 * M * N1 * K, "grouped gemm down": 2.0 * M * K * I}
     tflops = {n: round(f / (per[n] * 1e-6) / 1e12, 1) for n, f in gflops.items()}
     dom = max(gflops, key=lambda n: per[n])
@@ -222,6 +303,7 @@ def run_moe_ffn(args, torch, fq, dev):
         "data": "synthetic (seeded; shapes and distributions of the workload, no dataset)",
         "config": {"workload": WORKLOADS["moe_ffn"], "M": M, "hidden": K, "intermediate": I, "experts": G,
                    "buffer_sets": nsets},
+        **timing_fields(args, wall, t_dev, warm),
         "pct_fp8_peak_step": round(value / PEAK_FP8_TFLOPS * 100, 2),
         "kernels_us": {n: round(v, 2) for n, v in per.items()},
         "gemm_tflops": tflops,
@@ -268,7 +350,9 @@ def run_moe_layer(args, torch, fq, dev):
              "grouped gemm down", "combine"]
     disp = {}
 
-    def step(s, ev=None):
+    def step(i, ev=None):
+        s = sets[i % nsets]
+
         def dispatch():
             disp["r"] = fq.fp8q_moe_dispatch(ids, s["xq"], s["sa"], cfg["e_begin"], G, capacity=R, stream=stream)
         calls = [
@@ -290,20 +374,13 @@ def run_moe_layer(args, torch, fq, dev):
         if ev is not None:
             ev[len(calls)].record(stream)
 
-    for i in range(args.warmup):
-        step(sets[i % nsets])
+    step(0)
     torch.cuda.synchronize()
     got_rows = int(disp["r"][2][-1].item())
     if got_rows != R:
         raise RuntimeError(f"dispatch produced {got_rows} rows, expected {R}")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(sets[i % nsets], evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)])) * 1e3
-           for j, n in enumerate(names)}
+    wall, t_dev, per_l, warm = run_steps(torch, args, step, len(names))
+    per = dict(zip(names, per_l))
     gflops = {"grouped gemm up": 2.0 * R * N1 * K, "grouped gemm down": 2.0 * R * K * I}
     tflops = {n: round(f / (per[n] * 1e-6) / 1e12, 1) for n, f in gflops.items()}
     dom = max(gflops, key=lambda n: per[n])
@@ -317,6 +394,7 @@ def run_moe_layer(args, torch, fq, dev):
         "data": "synthetic (seeded; shapes and distributions of the workload, no dataset)",
         "config": {"workload": WORKLOADS["moe_layer"], "tokens": T, "rows": R, "hidden": K, "intermediate": I,
                    "experts": G, "buffer_sets": nsets},
+        **timing_fields(args, wall, t_dev, warm),
         "pct_fp8_peak_step": round(value / PEAK_FP8_TFLOPS * 100, 2),
         "kernels_us": {n: round(v, 2) for n, v in per.items()},
         "gemm_tflops": tflops,
@@ -358,7 +436,8 @@ def run_train(args, torch, fq, dev):
     stream = torch.cuda.current_stream()
     names = ["quant_act_dual(X)", "quant_w_t(W)", "gemm fwd", "quant_act_dual(dY)", "gemm dgrad", "gemm_rowscaled wgrad"]
 
-    def step(s, ev=None):
+    def step(i, ev=None):
+        s = sets[i % nsets]
         calls = [
             lambda: fq.fp8q_quantize_act_dual(s["x"], s["xq"], s["sa"], s["xqt"], s["sat"], stream=stream),
             lambda: fq.fp8q_quantize_w_128x128_t(s["w"], s["wq"], s["sb"], s["wqt"], s["sbt"], stream=stream),
@@ -374,17 +453,8 @@ def run_train(args, torch, fq, dev):
         if ev is not None:
             ev[len(calls)].record(stream)
 
-    for i in range(args.warmup):
-        step(sets[i % nsets])
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(sets[i % nsets], evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)])) * 1e3
-           for j, n in enumerate(names)}
+    wall, t_dev, per_l, warm = run_steps(torch, args, step, len(names))
+    per = dict(zip(names, per_l))
     gemm_flops = 2.0 * M * N * K
     tflops = {n: round(gemm_flops / (per[n] * 1e-6) / 1e12, 1) for n in names if n.startswith("gemm")}
     dom = max((n for n in names if n.startswith("gemm")), key=lambda n: per[n])
@@ -395,6 +465,7 @@ def run_train(args, torch, fq, dev):
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3 (fp32 accumulate)",
         "data": "synthetic (seeded; shapes and distributions of the workload, no dataset)",
         "config": {"workload": WORKLOADS["train"], "M": M, "N": N, "K": K, "buffer_sets": nsets},
+        **timing_fields(args, wall, t_dev, warm),
         "pct_fp8_peak_step": round(value / PEAK_FP8_TFLOPS * 100, 2),
         "kernels_us": {n: round(v, 2) for n, v in per.items()},
         "gemm_tflops": tflops,
@@ -469,56 +540,38 @@ def main():
 
     fused = args.quant == "fused"
 
-    def quantize(s, ev=None):
-        # ev: events recorded after the activation and after the weight quantization
-        if fused:
-            fq.fp8q_quantize_act_w(s["x"], s["w"], xq=s["xq"], sa=s["sa"], wq=s["wq"], sb=s["sb"], stream=stream)
-            if ev is not None:
-                ev[0].record(stream)
-                ev[1].record(stream)
-        else:
-            fq.fp8q_quantize_act_1x128(s["x"], xq=s["xq"], sa=s["sa"], stream=stream)
-            if ev is not None:
-                ev[0].record(stream)
-            fq.fp8q_quantize_w_128x128(s["w"], wq=s["wq"], sb=s["sb"], stream=stream)
-            if ev is not None:
-                ev[1].record(stream)
-
-    def step(s):
-        quantize(s)
+    def gemm(s):
         if grouped:
             fq.fp8q_grouped_gemm_blockscaled(s["xq"], s["sa"], s["wq"], s["sb"], off_d, out=s["c"], stream=stream)
         else:
             fq.fp8q_gemm_blockscaled(s["xq"], s["sa"], s["wq"], s["sb"], out=s["c"], stream=stream)
 
-    for i in range(args.warmup):
-        step(sets[i % nsets])
-        if cal_src is not None:
-            cal_dst.copy_(cal_src)
-    torch.cuda.synchronize()
-
-    K_steps = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K_steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K_steps):
+    def step(i, ev=None):
         s = sets[i % nsets]
-        e = evs[i]
-        e[0].record(stream)
-        quantize(s, (e[1], e[2]))
-        if grouped:
-            fq.fp8q_grouped_gemm_blockscaled(s["xq"], s["sa"], s["wq"], s["sb"], off_d, out=s["c"], stream=stream)
+        if fused:
+            calls = [lambda: fq.fp8q_quantize_act_w(s["x"], s["w"], xq=s["xq"], sa=s["sa"], wq=s["wq"], sb=s["sb"],
+                                                    stream=stream)]
         else:
-            fq.fp8q_gemm_blockscaled(s["xq"], s["sa"], s["wq"], s["sb"], out=s["c"], stream=stream)
-        e[3].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+            calls = [lambda: fq.fp8q_quantize_act_1x128(s["x"], xq=s["xq"], sa=s["sa"], stream=stream),
+                     lambda: fq.fp8q_quantize_w_128x128(s["w"], wq=s["wq"], sb=s["sb"], stream=stream)]
+        calls.append(lambda: gemm(s))
+        for j, c in enumerate(calls):
+            if ev is not None:
+                ev[j].record(stream)
+            c()
+        if ev is not None:
+            ev[len(calls)].record(stream)
+        if cal_src is not None and ev is None and i < args.warmup:
+            cal_dst.copy_(cal_src)  # counter calibration: a plain copy right after a GEMM
+
+    wall, t_dev, per, warm = run_steps(torch, args, step, 2 if fused else 3)
+    K_steps = args.steps
     if cal_src is not None:
         for _ in range(3):
             cal_dst.copy_(cal_src)
         torch.cuda.synchronize()
 
-    # Outside the timed region: each quantizer in its own launch, for the per-quantizer
+    # After the timed phases: each quantizer in its own launch, for the per-quantizer
     # figures (in fused mode the timed steps run them as one launch).
     sep = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(10)]
     for i, e in enumerate(sep):
@@ -532,14 +585,11 @@ def main():
     s_act = float(np.mean([e[0].elapsed_time(e[1]) for e in sep])) * 1e-3
     s_w = float(np.mean([e[1].elapsed_time(e[2]) for e in sep])) * 1e-3
 
-    t_act = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in range(K_steps)]) * 1e-3
-    t_w = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in range(K_steps)]) * 1e-3
-    t_g = np.array([evs[i][2].elapsed_time(evs[i][3]) for i in range(K_steps)]) * 1e-3
-    t_dev = evs[0][0].elapsed_time(evs[-1][3]) * 1e-3
     ms_per_step = wall / K_steps * 1e3
     value = flops * K_steps / wall / 1e12
 
-    a_act, a_w, a_g = t_act.mean(), t_w.mean(), t_g.mean()
+    # per-launch means (microseconds) from the kernel-timing pass, in seconds
+    a_act, a_w, a_g = (per[0] * 1e-6, 0.0, per[1] * 1e-6) if fused else (per[0] * 1e-6, per[1] * 1e-6, per[2] * 1e-6)
     gemm_tflops = flops / a_g / 1e12
     traffic = measured_traffic(args.workload)
     roofline = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
@@ -567,6 +617,7 @@ def main():
         "data": "synthetic (seeded; shapes and distributions of the workload, no dataset)",
         "config": {"workload": WORKLOADS[args.workload], "M": M, "N": N, "K": K, "experts": G,
                    "out": cfg["out_dtype"], "buffer_sets": nsets},
+        **timing_fields(args, wall, t_dev, warm),
         "pct_fp8_peak_step": round(value / PEAK_FP8_TFLOPS * 100, 2),
         "gemm_only_tflops": round(gemm_tflops, 1),
         # act quant (its own launch) + GEMM only, the weights quantized in a separate call
@@ -574,7 +625,7 @@ def main():
         "quant": args.quant,
         "kernels_us": ({"quantize_act_w (fused)": round(a_act * 1e6, 2)} if fused else
                        {"quantize_act_1x128": round(a_act * 1e6, 2), "quantize_w_128x128": round(a_w * 1e6, 2)})
-        | {"gemm": round(a_g * 1e6, 2), "device_span_per_step": round(t_dev / K_steps * 1e6, 2),
+        | {"gemm": round(a_g * 1e6, 2),
            "separate launches, untimed: quantize_act_1x128": round(s_act * 1e6, 2),
            "separate launches, untimed: quantize_w_128x128": round(s_w * 1e6, 2)},
         "quant_GBs": ({"act_w": round((bytes_act + bytes_w) / a_act / 1e9, 1),
@@ -584,6 +635,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if args.vendor_context and not grouped:
+        line["vendor_context"] = vendor_context(torch, M, N, K, K_steps)
     if not args.no_cpu_baseline and int(os.environ.get("RANK", "0")) == 0:
         line["cpu_baseline"] = cpu_baseline(cfg, flops)
     print(json.dumps(line), flush=True)
