@@ -37,7 +37,9 @@ back, bracketed by a device synchronize and HIP events on the kernels' stream, n
 recorded between the kernels; (3) the kernel-timing pass: K more steps, identical but with
 a HIP event recorded on the kernels' stream between consecutive launches, which gives each
 kernel's average launch duration (each event adds a marker between two kernels, which is
-why the timed region records none).  `roofline` describes the dominant kernel (the
+why the timed region records none); (4) unless --clock-seconds 0, untimed steps for two more
+seconds while amdsmi samples the graphics clock and socket power (its metrics refresh about
+once a second), which gives the FP8 peak at the clock the step actually runs at.  `roofline` describes the dominant kernel (the
 GEMM): algorithmic FLOPs per launch / its average duration, against the 5.0 PFLOP/s dense
 FP8 peak.  `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 """
@@ -84,6 +86,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="continue the untimed warm-up steps until this many ms of them have run")
+    ap.add_argument("--clock-seconds", type=float, default=2.0,
+                    help="after the timed phases, run untimed steps this long and sample the GPU clock and "
+                         "socket power (amdsmi) during the second half; 0 skips it")
     ap.add_argument("--workload", default="dense", choices=sorted(WORKLOADS))
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0: enough to exceed the 256 MB cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -152,14 +157,64 @@ def run_steps(torch, args, step, n_calls):
     torch.cuda.synchronize()
     per = [float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K_steps)])) * 1e3
            for j in range(n_calls)]
+    args.clock = sustained_clock(torch, args, step, n + 2 * K_steps)
     return wall, t_dev, per, n
+
+
+def sustained_clock(torch, args, step, first):
+    """Median graphics clock (mean over the XCDs) and socket power that amdsmi reports while
+    back-to-back steps run, sampled in the second half of --clock-seconds of steps; None when
+    skipped, a reason string when amdsmi is unavailable."""
+    if args.clock_seconds <= 0:
+        return None
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception as ex:  # pragma: no cover - depends on the machine
+        return f"unavailable: {type(ex).__name__}"
+    clocks, power = [], []
+    try:
+        t0 = time.perf_counter()
+        i, last = first, 0.0
+        while time.perf_counter() - t0 < args.clock_seconds:
+            step(i, None)
+            i += 1
+            if (i - first) % 10 == 0:
+                torch.cuda.synchronize()
+                now = time.perf_counter() - t0
+                if now > args.clock_seconds / 2 and now - last > 0.1:
+                    last = now
+                    m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+                    per_xcd = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float))]
+                    clk = float(np.mean(per_xcd)) if per_xcd else m.get("current_gfxclk")
+                    if isinstance(clk, (int, float)):
+                        clocks.append(float(clk))
+                    if isinstance(m.get("current_socket_power"), (int, float)):
+                        power.append(float(m["current_socket_power"]))
+        torch.cuda.synchronize()
+    finally:
+        amdsmi.amdsmi_shut_down()
+    if not clocks:
+        return "unavailable: no clock samples"
+    clk = float(np.median(clocks))
+    return {"gfxclk_mhz": round(clk), "socket_power_w": round(float(np.median(power))) if power else None,
+            "samples": len(clocks), "fp8_peak_at_clock_tflops": round(PEAK_FP8_TFLOPS * clk / 2400.0, 1)}
 
 
 def timing_fields(args, wall, t_dev, warm):
     """The JSON fields that describe the timing phases."""
     return {"warmup_steps_run": warm, "settle_ms": args.settle_ms,
             "device_ms_per_step": round(t_dev / args.steps * 1e3, 4),
-            "kernel_timing": "HIP events between launches in a second pass of K identical steps"}
+            "kernel_timing": "HIP events between launches in a second pass of K identical steps",
+            "sustained_clock": args.clock}
+
+
+def at_clock(roofline, clock):
+    """Adds the dominant kernel's fraction of the FP8 peak at the sampled sustained clock."""
+    if isinstance(clock, dict) and roofline.get("unit") == "TFLOP/s":
+        roofline["frac_at_sustained_clock"] = round(roofline["achieved"] / clock["fp8_peak_at_clock_tflops"], 4)
+    return roofline
 
 
 def vendor_context(torch, M, N, K, steps):
@@ -308,9 +363,9 @@ def run_moe_ffn(args, torch, fq, dev):
         "kernels_us": {n: round(v, 2) for n, v in per.items()},
         "gemm_tflops": tflops,
         "swiglu_quant_GBs": round(h_bytes / (per["swiglu_quant(h)"] * 1e-6) / 1e9, 1),
-        "roofline": {"bound": "mfma", "achieved": tflops[dom], "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+        "roofline": at_clock({"bound": "mfma", "achieved": tflops[dom], "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops[dom] / PEAK_FP8_TFLOPS, 4), "traffic": None, "kernel": dom,
-                     "flop_per_launch": gflops[dom], "avg_launch_us": round(per[dom], 2)},
+                     "flop_per_launch": gflops[dom], "avg_launch_us": round(per[dom], 2)}, args.clock),
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
@@ -400,9 +455,9 @@ def run_moe_layer(args, torch, fq, dev):
         "gemm_tflops": tflops,
         "dispatch_GBs": round(disp_bytes / (per["dispatch"] * 1e-6) / 1e9, 1),
         "combine_GBs": round(comb_bytes / (per["combine"] * 1e-6) / 1e9, 1),
-        "roofline": {"bound": "mfma", "achieved": tflops[dom], "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+        "roofline": at_clock({"bound": "mfma", "achieved": tflops[dom], "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops[dom] / PEAK_FP8_TFLOPS, 4), "traffic": None, "kernel": dom,
-                     "flop_per_launch": gflops[dom], "avg_launch_us": round(per[dom], 2)},
+                     "flop_per_launch": gflops[dom], "avg_launch_us": round(per[dom], 2)}, args.clock),
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
@@ -469,9 +524,9 @@ def run_train(args, torch, fq, dev):
         "pct_fp8_peak_step": round(value / PEAK_FP8_TFLOPS * 100, 2),
         "kernels_us": {n: round(v, 2) for n, v in per.items()},
         "gemm_tflops": tflops,
-        "roofline": {"bound": "mfma", "achieved": tflops[dom], "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+        "roofline": at_clock({"bound": "mfma", "achieved": tflops[dom], "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops[dom] / PEAK_FP8_TFLOPS, 4), "traffic": None, "kernel": dom,
-                     "flop_per_launch": gemm_flops, "avg_launch_us": round(per[dom], 2)},
+                     "flop_per_launch": gemm_flops, "avg_launch_us": round(per[dom], 2)}, args.clock),
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
@@ -632,7 +687,7 @@ def main():
                        "act_w_frac_hbm": round((bytes_act + bytes_w) / a_act / 1e9 / PEAK_HBM_GBS, 4)} if fused else {})
         | {"act": round(bytes_act / s_act / 1e9, 1), "act_frac_hbm": round(bytes_act / s_act / 1e9 / PEAK_HBM_GBS, 4),
            "w": round(bytes_w / s_w / 1e9, 1), "w_frac_hbm": round(bytes_w / s_w / 1e9 / PEAK_HBM_GBS, 4)},
-        "roofline": roofline,
+        "roofline": at_clock(roofline, args.clock),
         "cpu_baseline": None,
     }
     if args.vendor_context and not grouped:
