@@ -119,6 +119,23 @@ def test_combine_random(in_dtype, out_dtype):
     combine_check(out, token_row, w, out_dtype)
 
 
+def test_combine_skips_rows_past_capacity():
+    """Slots whose row is at or past the expert outputs' row count (a dispatch that ran short
+    of capacity leaves -1, but any row >= capacity) contribute nothing, as if not local."""
+    rng = np.random.default_rng(13)
+    T, k, R, N = 40, 4, 64, 136
+    out = torch.from_numpy(rng.standard_normal((R, N)).astype(np.float32)).to(torch.bfloat16).cuda()
+    token_row = rng.integers(-1, R + 30, size=(T, k)).astype(np.int32)   # some rows >= R
+    w = rng.random((T, k)).astype(np.float32)
+    y = fq.fp8q_moe_combine(out, dev(token_row), dev(w), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    kept = np.where(token_row < R, token_row, -1).astype(np.int32)
+    used = host(out).astype(np.float64)
+    ref = om.combine(used, kept, w)
+    tol = k * 2.0 ** -23 * om.combine_bound(used, kept, w)
+    assert np.all(np.abs(host(y).astype(np.float64) - ref) <= tol)
+
+
 def test_moe_layer_full_size():
     """The moe_layer workload: 8192 tokens, top-8 of 256 experts, 32 local; dispatch
     bit-exact with the oracle, the same offsets as the workload's routing lists, the
