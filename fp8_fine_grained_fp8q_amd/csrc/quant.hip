@@ -310,31 +310,39 @@ __global__ __launch_bounds__(256) void quant_act_dual_kernel(const uint16_t *__r
   uint4 v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = load16_stream(x + base + (r0 + 16 * i) * K);
-  // every value widened to FP32 once, shared by both orientations
-  float xv[8][8];
+  // values stay packed (two BF16 per register) and are widened where used: one shift or
+  // mask each, which keeps the kernel small enough for 8 workgroups per CU
+  auto xv = [&](int i, int e) { return bf16_elem(v[i], e); };
+  // An empty asm that claims to modify the packed words: the widened values of one phase
+  // then cannot be kept for the next one, and are recomputed (one shift or mask each)
+  // instead of taking 64 registers across the phases.
+  auto fence_values = [&]() {
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) xv[i][e] = bf16_elem(v[i], e);
+    for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(v[i].x), "+v"(v[i].y), "+v"(v[i].z), "+v"(v[i].w));
+  };
 
   // Row tiles (1x128 along K): the forward codes.
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    float m = fabsf(xv[i][0]);
+    float xr[8];
 #pragma unroll
-    for (int e = 1; e < 8; ++e) m = fmaxf(m, fabsf(xv[i][e]));
+    for (int e = 0; e < 8; ++e) xr[e] = xv(i, e);
+    float m = fabsf(xr[0]);
+#pragma unroll
+    for (int e = 1; e < 8; ++e) m = fmaxf(m, fabsf(xr[e]));
     const float s = row16_max(m) / kE4M3Max;
-    *reinterpret_cast<uint2 *>(xq + base + (r0 + 16 * i) * K) = quant8f<true>(xv[i], GroupDiv(s));
+    *reinterpret_cast<uint2 *>(xq + base + (r0 + 16 * i) * K) = quant8f<true>(xr, GroupDiv(s));
     if (sub == 0) sa[kb * M + mb * 128 + r0 + 16 * i] = s;
   }
 
   // Column tiles (128 tokens of one channel).
+  fence_values();
   float cm[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    float m = fabsf(xv[0][e]);
+    float m = fabsf(xv(0, e));
 #pragma unroll
-    for (int i = 1; i < 8; ++i) m = fmaxf(m, fabsf(xv[i][e]));
+    for (int i = 1; i < 8; ++i) m = fmaxf(m, fabsf(xv(i, e)));
     m = fmaxf(m, __shfl_xor(m, 16));
     m = fmaxf(m, __shfl_xor(m, 32));
     cm[e] = m;
@@ -354,15 +362,14 @@ __global__ __launch_bounds__(256) void quant_act_dual_kernel(const uint16_t *__r
     sat[mb * K + kb * 128 + tid] = s;
   }
   __syncthreads();
+  fence_values();
   float cs[8], cr[8];
-  int cmode[8];
   bool all_fast = true;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     cs[e] = colscale[sub * 8 + e];
     cr[e] = colrcp[sub * 8 + e];
-    cmode[e] = colmode[sub * 8 + e];
-    all_fast = all_fast && cmode[e] == 1;
+    all_fast = all_fast && colmode[sub * 8 + e] == 1;
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -373,9 +380,9 @@ __global__ __launch_bounds__(256) void quant_act_dual_kernel(const uint16_t *__r
         GroupDiv d(0.0f);
         d.s = cs[e];
         d.r = cr[e];
-        y[e] = d.fast_bf16(xv[i][e]);
+        y[e] = d.fast_bf16(xv(i, e));
       } else {
-        y[e] = div_any(xv[i][e], cs[e], cr[e], cmode[e]);
+        y[e] = div_any(xv(i, e), cs[e], cr[e], colmode[sub * 8 + e]);
       }
     }
     uint2 q;
