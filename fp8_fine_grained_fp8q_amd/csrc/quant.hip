@@ -194,6 +194,11 @@ __device__ __forceinline__ void quant_w_block(int64_t bid, const uint16_t *__res
   const float amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
   const float s = amax / kE4M3Max;
   const GroupDiv dv(s);
+  // An empty asm claiming to modify the packed values: the amax pass's widened values are
+  // recomputed below (one shift or mask each) rather than held in 64 registers across the
+  // barrier, so more workgroups fit per CU.
+#pragma unroll
+  for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(v[i].x), "+v"(v[i].y), "+v"(v[i].z), "+v"(v[i].w));
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const uint2 q = quant8(v[i], dv);
