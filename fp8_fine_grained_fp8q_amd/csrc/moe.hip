@@ -107,7 +107,8 @@ __global__ __launch_bounds__(kRouteThreads) void moe_scan_kernel(int64_t n, int6
   const int g = tid / E, e = tid % E;
   const int64_t c_lo = g < G ? g * per : C, c_hi = c_lo + per < C ? c_lo + per : C;
   int s = 0;
-  for (int64_t c = c_lo; c < c_hi; ++c) s += token_row[c * kChunk + e];
+#pragma unroll 8
+  for (int64_t c = c_lo; c < c_hi; ++c) s += token_row[c * kChunk + e];  // independent loads
   if (g < G) part[tid] = s;
   __syncthreads();
   int tot = 0;
@@ -127,6 +128,7 @@ __global__ __launch_bounds__(kRouteThreads) void moe_scan_kernel(int64_t n, int6
   if (tid == 0) offsets[E] = all;
   __syncthreads();
   int base = g < G ? first[e] + part[tid] : 0;
+#pragma unroll 8
   for (int64_t c = c_lo; c < c_hi; ++c) {
     const int v = token_row[c * kChunk + e];
     token_row[c * kChunk + e] = base;

@@ -45,11 +45,11 @@ def assert_dispatch_equal(got, ref):
 
 # The routing works in chunks of 1024 (token, slot) entries, the last taking the remainder
 # (one chunk below 2048 entries): lone chunks, two chunks with a two-round tail, many chunks
-# per scan thread (C > 1024 / E), E = 1024 (one scan thread per expert), E = 1.
+# per scan thread (C > 1024 / E), E = 1024 (one scan thread per expert, 2 and 32 chunks), E = 1.
 @pytest.mark.parametrize("T,k,E,e_begin,K,id_range", [(300, 8, 20, 16, 384, 64), (77, 1, 5, 0, 128, 64),
                                                       (129, 3, 64, 0, 256, 64), (64, 6, 1, 9, 128, 64),
                                                       (4100, 8, 512, 100, 128, 1024), (300, 8, 1024, 0, 128, 1500),
-                                                      (2048, 1, 1, 3, 128, 8)])
+                                                      (2048, 1, 1, 3, 128, 8), (4096, 8, 1024, 0, 128, 2048)])
 def test_dispatch_random(T, k, E, e_begin, K, id_range):
     rng = np.random.default_rng(T * 31 + k * 7 + E)
     x = wl.bf16_bits(rng.standard_normal((T, K), dtype=np.float32) * np.float32(4.0))
