@@ -1,9 +1,11 @@
-// C ABI of libfp8q (see include/fp8q.h): argument checks, then one kernel launch per call.
+// C ABI of libfp8q (see include/fp8q.h): argument checks, then the call's kernel launches.
 // Every check runs before the first HIP call, so a bad call never touches the device.
 #include "fp8q.h"
 
 #include <hip/hip_runtime.h>
 #include <stdlib.h>
+
+#include <mutex>
 
 #include "fp8q_launch.h"
 
@@ -100,6 +102,9 @@ fp8q_status fp8q_grouped_gemm_blockscaled(const uint8_t *xq, const float *sa, co
   if (misaligned(offsets, 4)) return FP8Q_ERR_ALIGN;
   if (device_ok() != FP8Q_OK) return FP8Q_ERR_DEVICE;
   if (debug_checks()) {
+    // One device flag serves the check: checks from several threads run one at a time.
+    static std::mutex check_mutex;
+    std::lock_guard<std::mutex> lock(check_mutex);
     bool bad = false;
     if (fp8q::check_grouped_offsets(offsets, G, M_tot, as_stream(stream), &bad) != hipSuccess)
       return FP8Q_ERR_LAUNCH;

@@ -41,9 +41,11 @@
  *    take K (the contraction length) up to 4 194 304 (2^22): their kernels address the
  *    operand stages with 32-bit offsets; larger K returns FP8Q_ERR_SHAPE.
  *  - The library allocates no device memory; its only global state is a per-device
- *    cache of the CU count (written once, the same value by any thread): calls are
- *    reentrant and thread-safe.  Kernel faults surface at the caller's next
- *    synchronization of `stream`.
+ *    cache of the CU count (written once, the same value by any thread) and the
+ *    device flag of the grouped GEMM's offsets check, used only under FP8Q_DEBUG
+ *    (the library runs those checks one at a time): calls are reentrant and
+ *    thread-safe.  Kernel faults surface at the caller's next synchronization of
+ *    `stream`.
  *  - The dense GEMMs pick their tile plan from the shape and the CU count; the
  *    environment variable FP8Q_DENSE_SPLIT ("off", or a count a of 256-wide tile
  *    columns) overrides it for testing.  Every plan gives bit-identical results.
