@@ -151,7 +151,7 @@ __global__ __launch_bounds__(kRouteThreads) void moe_rank_kernel(const int32_t *
   __shared__ int32_t run[kMaxLocalExperts];                  // the chunk's next row, per expert
   __shared__ int32_t wcnt[kRouteWaves * kMaxLocalExperts];   // a round's count per wave and expert
   __shared__ int32_t ws[kRouteWaves];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, wave = tid >> 6;
   int64_t lo, hi;
   chunk_range(blockIdx.x, C, n, lo, hi);
   for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) wcnt[i] = 0;
