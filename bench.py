@@ -155,8 +155,10 @@ def run_steps(torch, args, step, n_calls):
     for i in range(K_steps):
         step(n + K_steps + i, evs[i])
     torch.cuda.synchronize()
-    per = [float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K_steps)])) * 1e3
-           for j in range(n_calls)]
+    samples = [[evs[i][j].elapsed_time(evs[i][j + 1]) * 1e3 for i in range(K_steps)] for j in range(n_calls)]
+    per = [float(np.mean(v)) for v in samples]
+    args.launch_stats = [{"median": round(float(np.median(v)), 2), "p10": round(float(np.percentile(v, 10)), 2),
+                          "p90": round(float(np.percentile(v, 90)), 2)} for v in samples]
     args.clock = sustained_clock(torch, args, step, n + 2 * K_steps)
     return wall, t_dev, per, n
 
@@ -225,11 +227,13 @@ def sustained_clock(torch, args, step, first):
             "samples": len(clocks), "fp8_peak_at_clock_tflops": round(PEAK_FP8_TFLOPS * clk / 2400.0, 1)}
 
 
-def timing_fields(args, wall, t_dev, warm):
-    """The JSON fields that describe the timing phases."""
+def timing_fields(args, wall, t_dev, warm, names):
+    """The JSON fields that describe the timing phases, with the median and the 10th / 90th
+    percentiles of each kernel's launch durations in the kernel-timing pass."""
     return {"warmup_steps_run": warm, "settle_ms": args.settle_ms,
             "device_ms_per_step": round(t_dev / args.steps * 1e3, 4),
             "kernel_timing": "HIP events between launches in a second pass of K identical steps",
+            "kernels_us_median_p10_p90": dict(zip(names, args.launch_stats)),
             "sustained_clock": args.clock}
 
 
@@ -273,6 +277,36 @@ def vendor_context(torch, M, N, K, steps):
     return out
 
 
+def hbm_ceiling(torch, stream, sizes):
+    """GB/s of two plain streaming kernels (libfp8q_probe.so) at the quantizers' input sizes:
+    a 16-byte-per-lane copy, and a read of BF16 words writing one byte per value (the
+    quantizers' 2:1 read/write mix, no arithmetic).  20 back-to-back launches rotated over
+    copies larger than the Infinity Cache, as for the quantizers' own figures."""
+    import ctypes
+    path = os.path.join(ROOT, "fp8_fine_grained_fp8q_amd", "libfp8q_probe.so")
+    if not os.path.exists(path):
+        return "unavailable: libfp8q_probe.so not built"
+    lib = ctypes.CDLL(path)
+    for f in (lib.probe_copy, lib.probe_read2_write1):
+        f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        f.restype = ctypes.c_int
+    out = {}
+    for label, nbytes in sizes.items():
+        n16 = nbytes // 16
+        src = torch.empty(n16 * 16, dtype=torch.uint8, device="cuda").fill_(0x3c)
+        for kind, fn, wbytes in (("copy", lib.probe_copy, n16 * 16), ("read2_write1", lib.probe_read2_write1, n16 * 8)):
+            def launch(a, d):
+                rc = fn(a.data_ptr(), d.data_ptr(), n16, stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"probe launch failed ({rc})")
+            t = separate_launch_time(torch, stream, src, launch,
+                                     lambda: torch.empty(wbytes, dtype=torch.uint8, device="cuda"))
+            moved = n16 * 16 + wbytes
+            out[f"{label}_{kind}_GBs"] = round(moved / t / 1e9, 1)
+        del src
+    return out
+
+
 def cpu_baseline(cfg, flops_step):
     """The oracle as it stands, on a bounded sample of the workload (rank 0 only)."""
     from oracle import gemm as og
@@ -282,6 +316,10 @@ def cpu_baseline(cfg, flops_step):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         threads = 1
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):  # pragma: no cover
+        affinity = None
     x, w, offsets = cfg["x"], cfg["w"], cfg["offsets"]
     M, K = x.shape
     G, N, _ = w.shape
@@ -314,8 +352,11 @@ def cpu_baseline(cfg, flops_step):
         t_step = (t1 - t0) * rows_scale + (t2 - t1) * G + (t3 - t2) * rows_scale
         sample = (f"oracle on expert {g} ({hi - lo} rows): act quant and GEMM extrapolated x{rows_scale:.3g} "
                   f"to {M} rows, weight quant x{G} experts")
+    # cores: the BLAS threads the oracle's FP64 product runs on (its quantizers are
+    # single-threaded numpy); the host's CPU count and this process's affinity alongside
     return {"value": flops_step / t_step / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": sample, "seconds_measured": round(t3 - t0, 2), "seconds_per_step": round(t_step, 2)}
+            "sample": sample, "seconds_measured": round(t3 - t0, 2), "seconds_per_step": round(t_step, 2),
+            "blas_threads": int(threads), "host_cpus": os.cpu_count(), "affinity_cpus": affinity}
 
 
 def run_moe_ffn(args, torch, fq, dev):
@@ -381,7 +422,7 @@ def run_moe_ffn(args, torch, fq, dev):
         "data": "synthetic (seeded; shapes and distributions of the workload, no dataset)",
         "config": {"workload": WORKLOADS["moe_ffn"], "M": M, "hidden": K, "intermediate": I, "experts": G,
                    "buffer_sets": nsets},
-        **timing_fields(args, wall, t_dev, warm),
+        **timing_fields(args, wall, t_dev, warm, names),
         "pct_fp8_peak_step": round(value / PEAK_FP8_TFLOPS * 100, 2),
         "kernels_us": {n: round(v, 2) for n, v in per.items()},
         "gemm_tflops": tflops,
@@ -472,7 +513,7 @@ def run_moe_layer(args, torch, fq, dev):
         "data": "synthetic (seeded; shapes and distributions of the workload, no dataset)",
         "config": {"workload": WORKLOADS["moe_layer"], "tokens": T, "rows": R, "hidden": K, "intermediate": I,
                    "experts": G, "buffer_sets": nsets},
-        **timing_fields(args, wall, t_dev, warm),
+        **timing_fields(args, wall, t_dev, warm, names),
         "pct_fp8_peak_step": round(value / PEAK_FP8_TFLOPS * 100, 2),
         "kernels_us": {n: round(v, 2) for n, v in per.items()},
         "gemm_tflops": tflops,
@@ -543,7 +584,7 @@ def run_train(args, torch, fq, dev):
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3 (fp32 accumulate)",
         "data": "synthetic (seeded; shapes and distributions of the workload, no dataset)",
         "config": {"workload": WORKLOADS["train"], "M": M, "N": N, "K": K, "buffer_sets": nsets},
-        **timing_fields(args, wall, t_dev, warm),
+        **timing_fields(args, wall, t_dev, warm, names),
         "pct_fp8_peak_step": round(value / PEAK_FP8_TFLOPS * 100, 2),
         "kernels_us": {n: round(v, 2) for n, v in per.items()},
         "gemm_tflops": tflops,
@@ -660,6 +701,8 @@ def main():
         lambda x, w, d: fq.fp8q_quantize_act_w(x, w, xq=d[0], sa=d[1], wq=d[2], sb=d[3], stream=stream),
         lambda: tuple(torch.empty_like(sets[0][k]) for k in ("xq", "sa", "wq", "sb")))
 
+    ceiling = hbm_ceiling(torch, stream, {"x_bf16": 2 * M * K, "w_bf16": 2 * G * N * K})
+
     ms_per_step = wall / K_steps * 1e3
     value = flops * K_steps / wall / 1e12
 
@@ -692,7 +735,9 @@ def main():
         "data": "synthetic (seeded; shapes and distributions of the workload, no dataset)",
         "config": {"workload": WORKLOADS[args.workload], "M": M, "N": N, "K": K, "experts": G,
                    "out": cfg["out_dtype"], "buffer_sets": nsets},
-        **timing_fields(args, wall, t_dev, warm),
+        **timing_fields(args, wall, t_dev, warm,
+                        (["quantize_act_w (fused)"] if fused else ["quantize_act_1x128", "quantize_w_128x128"])
+                        + ["gemm"]),
         "pct_fp8_peak_step": round(value / PEAK_FP8_TFLOPS * 100, 2),
         "gemm_only_tflops": round(gemm_tflops, 1),
         # act quant (its own launch) + GEMM only, the weights quantized in a separate call
@@ -713,6 +758,8 @@ def main():
            "act_w_own_frac_hbm": round((bytes_act + bytes_w) / s_fused / 1e9 / PEAK_HBM_GBS, 4),
            "act": round(bytes_act / s_act / 1e9, 1), "act_frac_hbm": round(bytes_act / s_act / 1e9 / PEAK_HBM_GBS, 4),
            "w": round(bytes_w / s_w / 1e9, 1), "w_frac_hbm": round(bytes_w / s_w / 1e9 / PEAK_HBM_GBS, 4)},
+        # what plain streaming kernels of the same sizes reach on this device (achievable ceiling)
+        "hbm_ceiling": ceiling,
         "roofline": at_clock(roofline, args.clock),
         "cpu_baseline": None,
     }

@@ -20,6 +20,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfp8q.so")
 SOURCES = ["quant.hip", "gemm.hip", "moe.hip", "fp8q_abi.cpp"]
+# Streaming-bandwidth probes the benchmark reads the quantizers against (not part of the path).
+PROBE_LIB = os.path.join(HERE, "libfp8q_probe.so")
+PROBE_SOURCES = ["stream_probe.hip"]
 ARCH = "gfx950"
 
 
@@ -31,12 +34,18 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
+    _compile(SOURCES, LIB, verbose)
+    _compile(PROBE_SOURCES, PROBE_LIB, verbose)
+    return LIB
+
+
+def _compile(sources, lib, verbose):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Wall", "-Wno-unused-function",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-I", INCLUDE, "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+           *[os.path.join(CSRC, s) for s in sources], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -46,8 +55,7 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
 
 
 if __name__ == "__main__":

@@ -19,8 +19,11 @@ Readings:
   the oracle's where h/s lies within a few FP32 ulps of an E4M3 rounding boundary, and a
   tile scale by a few ulps; the parity tests compare on those terms.
 
-Parity status: pinned (SiLU identities and printed values, the composition with the pinned
-quantizer, extreme arguments).
+Parity status: pinned -- SiLU by its identities, printed logistic values and extreme
+arguments; the FP32-input 1x128 quantizer by the exact-rational brute force on full-precision
+FP32 tiles (24-bit significands) and on zero, -0, FP32-subnormal, power-of-two and constant
+tiles, with a tile on which dividing and multiplying by RN(1/s) give different codes and
+random tiles on which rounding the values to BF16 first changes codes.
 """
 from __future__ import annotations
 
