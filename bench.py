@@ -126,6 +126,24 @@ def measured_traffic(workload: str):
     return t.get("workloads", {}).get(workload, {}).get("bytes_per_launch")
 
 
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemm_counters.json")
+
+
+def measured_counters(kernel_substring: str):
+    """Matrix-core busy, vector-ALU busy and LDS figures of the GEMM from the committed
+    counter summary (fp8_fine_grained_fp8q_amd/counter_summary.py), only if it was taken on
+    the current GEMM source; else None."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            entry = json.load(f).get(kernel_substring)
+    except (OSError, ValueError):
+        return None
+    if not entry or entry.get("gemm_source_sha256_16") != source_hash():
+        return None
+    keys = ("mfma_busy", "valu_busy", "coexec", "lds_bank_conflict", "wait_lds_share", "clock_ghz_from_gui")
+    return {k: entry[k] for k in keys if k in entry}
+
+
 def run_steps(torch, args, step, n_calls):
     """The three timing phases (module docstring) around `step(i, ev)`, which launches step
     i's kernels on the current stream, recording ev[j] before its j-th launch and ev[n_calls]
@@ -715,6 +733,9 @@ def main():
                 "kernel": "gemm_grouped_kernel" if grouped else "gemm_blockscaled_split_kernel<8, 6, false>",
                 "flop_per_launch": flops, "avg_launch_us": round(a_g * 1e6, 2),
                 "algorithmic_bytes_per_launch": bytes_gemm}
+    counters = measured_counters("gemm_grouped_kernel" if grouped else "gemm_")
+    if counters:
+        roofline["counters"] = counters
     if grouped:
         # the expert-weight stream bounds the grouped GEMM: report the HBM view as well
         roofline["hbm_achieved_GBs"] = round(bytes_gemm / a_g / 1e9, 1)

@@ -7,6 +7,9 @@
 
 namespace fp8q {
 
+// Compute units of the current device (cached per device; 256 if the query fails).
+int device_cu_count();
+
 hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, uint8_t *xq, float *sa,
                             hipStream_t stream);
 

@@ -411,6 +411,315 @@ __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Ping-pong schedule for 256 x 256 tiles.  The two waves that share a SIMD (wave w and
+// w + 4) take turns: while one multiplies operands it already holds in registers, the
+// other reads its next operands from LDS, and they swap at every workgroup barrier.  The
+// waves 0-3 run one phase ahead of the waves 4-7, so in every phase each SIMD has one wave
+// feeding its matrix core and the LDS reads never sit between a barrier and the first MFMA.
+//
+// Each wave owns 64 rows x 128 columns as before.  A K block is four phases for a wave:
+//   M0: read the activation fragments (4 row groups) and the weight fragments of its
+//       column half 0 (fragment columns 0-3),
+//   C0: 16 MFMAs (4 x 4 fragments) with the promotion FMAs in their shadow,
+//   M1: read the weight fragments of column half 1 (fragment columns 4-7),
+//   C1: 16 MFMAs and promotion.
+// The LDS stage is split into three regions: X (activation rows), W0 (the weight rows of
+// column half 0 of both wave columns) and W1 (half 1).  X and W0 are read only in M0
+// phases and W1 only in M1 phases, so with two buffers each region is free two phases after
+// its last read and its next copy (two K blocks ahead) gets about one and a half K blocks
+// of time to land: the copies of X and W0 for block kb + 2 are issued in M1(kb), those of
+// W1 for block kb + 1 in M0(kb), with the activation scales of block kb + 1.  Per K block a
+// wave issues 6 + 2 + 4 vector memory operations in that order, so fixed vmcnt counts name
+// exactly the copies that must have landed before the barrier preceding their first read.
+// Copies past the last K block read through an empty buffer resource (zeros, no memory
+// traffic) and keep the counts uniform.  Every wave waits for its own copies at the end of
+// its M phases (the loop body has no branch: a branch there lets the compiler move the
+// promotion FMAs out of the MFMA phases).
+// ---------------------------------------------------------------------------------------
+struct PPStages {
+  FP8Q_LDS uint8_t *x[2];   // 32 KB each: 256 activation rows
+  FP8Q_LDS uint8_t *w0[2];  // 16 KB each: weight rows of column half 0
+  FP8Q_LDS uint8_t *w1[2];  // 16 KB each: column half 1
+};
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Computes the 256 x (32 * NFR) tile t, NFR = 8 (256 wide) or 7 (224 wide): each wave owns
+// 64 rows x 16*NFR columns, C0 covers its fragment columns 0-3 and C1 columns 4 .. NFR-1.
+// The weight regions always hold 8 row groups; with NFR = 7 the last group of each wave
+// column in W1 is never read and its copies go through the empty resource.  kOne: every
+// wave's columns lie in one 128-column weight-scale block (256-wide tiles starting at a
+// multiple of 256), so a fragment row has one promotion scale per K block; otherwise each
+// fragment column picks the scale of its block.
+template <int NFR, bool kOne>
+__device__ __forceinline__ void gemm_tile_pp(const Tile &t, const float *__restrict__ sa, int64_t M, int64_t N,
+                                             int64_t K, void *__restrict__ c, int out_f32, const PPStages &st) {
+  static_assert(NFR == 7 || NFR == 8, "tile width 224 or 256");
+  static_assert(!kOne || NFR == 8, "one scale block per wave needs 128-column waves");
+  constexpr int kWN = 16 * NFR;  // columns per wave
+  constexpr int kNC1 = NFR - 4;  // fragment columns of C1
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool lead = wave < 4;  // waves 0-3 run one phase ahead
+  const int wm = wave >> 1;    // rows wm*64 .. +63
+  const int wn = wave & 1;     // cols wn*kWN .. +kWN-1
+  const int KB = static_cast<int>(K >> 7);
+  const int NB = static_cast<int>(N >> 7);
+  const int l16 = lane & 15;
+  const int kg = lane >> 4;
+
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(t.x + t.m_begin * K, static_cast<uint32_t>(t.rows * K));
+  const int rows_w = static_cast<int>(min(static_cast<int64_t>(2 * kWN), t.n_end - t.n0));
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(t.w + t.n0 * K, static_cast<uint32_t>(rows_w * K));
+  const __amdgpu_buffer_rsrc_t rnull = make_rsrc(t.x, 0u);
+  // Activation scales of the tile's rows: sa[kb][m_begin + r] at byte kb*M*4 + r*4; rows
+  // past the tile read other rows' (finite) scales or zeros, and only meet zero partials.
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(sa + t.m_begin, static_cast<uint32_t>(((KB - 1) * M + t.rows) * 4));
+
+  // Copies: every 1 KB block this wave moves lands on rows rowbase + 16*(block/2) of its
+  // region (the stage layout of lds_pos), so one per-lane offset serves all of them; the
+  // rest is a scalar offset.  X: blocks 8i + wave, tile rows 64i + rowbase.  Weight region
+  // r: blocks 8i + wave, tile rows kWN*i + 64r + rowbase (region group 4i + wave/2).
+  const int line = 4 * (wave & 1) + (lane >> 4);
+  const int rowbase = 16 * (wave >> 1) + line + 8 * ((lane >> 3) & 1);
+  const int voff = rowbase * static_cast<int>(K) + (((lane & 7) ^ line) << 4);
+  const bool w1_pad = (wave >> 1) >= kNC1;  // this wave's W1 blocks are the unused groups
+  const int fo0 = lds_pos(l16, 2 * kg), fo1 = lds_pos(l16, 2 * kg + 1);
+  const int sa_off = (wm * 64 + l16) * 4;  // + f*64 for fragment row f
+
+  // Weight-block scales: the wave's columns start in block nb0; fragment columns
+  // j >= jsplit lie in block nb0 + 1.
+  const int64_t wc0 = t.n0 + wn * kWN;
+  const int nb0 = static_cast<int>(min(static_cast<int64_t>(NB - 1), wc0 >> 7));
+  const int nb1 = min(NB - 1, nb0 + 1);
+  const int jsplit = kOne ? NFR : static_cast<int>((128 - (wc0 & 127)) >> 4);
+  const float *sbrow0 = t.sb + static_cast<int64_t>(nb0) * KB;
+  const float *sbrow1 = t.sb + static_cast<int64_t>(nb1) * KB;
+
+  v4f acc[4][NFR];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int j = 0; j < NFR; ++j) acc[f][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // X and W0 of block s into buffer s % 2 (6 loads), W1 of block s (2 loads), the lane's
+  // activation scales of block s (4 loads); blocks past the last read zeros / the last.
+  const int K32 = static_cast<int>(K);
+  auto copy_xw0 = [&](int s, auto buf) {
+    constexpr int b = decltype(buf)::value;
+    const bool ok = s < KB;
+    const __amdgpu_buffer_rsrc_t r_x = ok ? rx : rnull, r_w = ok ? rw : rnull;
+    const int koff = ok ? s * kBK : 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r_x, (FP8Q_LDS void *)(st.x[b] + (8 * i + wave) * 1024), 16, voff,
+                                               koff + 64 * i * K32, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r_w, (FP8Q_LDS void *)(st.w0[b] + (8 * i + wave) * 1024), 16, voff,
+                                               koff + kWN * i * K32, 0, 0);
+  };
+  auto copy_w1 = [&](int s, auto buf) {
+    constexpr int b = decltype(buf)::value;
+    const bool ok = s < KB && !w1_pad;
+    const __amdgpu_buffer_rsrc_t r_w = ok ? rw : rnull;
+    const int koff = ok ? s * kBK : 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r_w, (FP8Q_LDS void *)(st.w1[b] + (8 * i + wave) * 1024), 16, voff,
+                                               koff + (kWN * i + 64) * K32, 0, 0);
+  };
+  auto load_sa = [&](int s, float (&dst)[4]) {
+    const int so = (s < KB ? s : KB - 1) * static_cast<int>(M) * 4;
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+      dst[f] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsa, sa_off + 64 * f, so, 0));
+  };
+  // Phase boundary: this wave's LDS reads are complete (lgkmcnt(0)), then the workgroup
+  // barrier.  Written as one asm statement with a memory clobber rather than
+  // __syncthreads(), whose workgroup fence would also wait for every direct-to-LDS copy in
+  // flight (vmcnt(0)) and so drain the copy pipeline at every phase; the copies' own
+  // completion is covered by the vmcnt waits below.  Nothing is scheduled across it: the
+  // MFMAs carry no memory dependence and would otherwise drift into the neighbouring phase.
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Keeps the groups of vector memory operations in program order (the vmcnt counts name
+  // copies by their position in that order).
+  auto vm_order = [&]() { asm volatile("" ::: "memory"); };
+
+  v8i xf[4], wf[4];
+  v4f pp[4];       // partials of the last fragment column of the previous C phase
+  float sclp[4];   // their scales
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    pp[f] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    sclp[f] = 0.0f;
+  }
+  float saA[4], saB[4];
+  float sb0A = sbrow0[0], sb1A = kOne ? 0.0f : sbrow1[0], sb0B = 0.0f, sb1B = 0.0f;
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+
+  // Prologue: X/W0 of block 0, W1 of block 0, scales of block 0, X/W0 of block 1.
+  copy_xw0(0, B0{});
+  vm_order();
+  copy_w1(0, B0{});
+  vm_order();
+  load_sa(0, saA);
+  vm_order();
+  copy_xw0(1, B1{});
+  vm_wait<12>();  // X/W0 of block 0 landed (W1 0, the scales and X/W0 1 may be in flight)
+  barrier();
+  if (!lead) barrier();  // the lagging waves' first phase is idle
+
+  // C phase over fragment columns j0 .. j0+nc-1 with operands xf, wf; sc0 / sc1: this
+  // block's promotion scales of the columns before / from jsplit.
+  auto cphase = [&](int j0, int nc, const float (&sc0)[4], const float (&sc1)[4]) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      if (jj >= nc) break;
+      const int jp = jj == 0 ? (j0 == 0 ? NFR - 1 : j0 - 1) : j0 + jj - 1;  // column being folded
+      const bool first = jp < jsplit;                                       // wave-uniform
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const float sf = jj == 0 ? sclp[f] : (kOne || first ? sc0[f] : sc1[f]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[f][jp][i] = __builtin_fmaf(pp[f][i], sf, acc[f][jp][i]);
+        pp[f] = mfma_block(wf[jj], xf[f]);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // 4 VALU
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int jl = j0 + nc - 1;  // the column left for the next phase's first fold
+#pragma unroll
+    for (int f = 0; f < 4; ++f) sclp[f] = kOne || jl < jsplit ? sc0[f] : sc1[f];
+  };
+
+  // One K block kb in buffer buf = kb % 2: sac / sb*c its scales, san / sb*n receive block
+  // kb + 1's.
+  auto kstep = [&](int kb, auto buf, float (&sac)[4], float (&san)[4], float &sb0c, float &sb1c, float &sb0n,
+                   float &sb1n) {
+    constexpr int b = decltype(buf)::value;
+    using Next = std::integral_constant<int, 1 - b>;
+    // M0
+    vm_order();
+    copy_w1(kb + 1, Next{});
+    vm_order();
+    load_sa(kb + 1, san);
+    vm_order();
+    const int kn = kb + 1 < KB ? kb + 1 : KB - 1;
+    sb0n = sbrow0[kn];
+    if (!kOne) sb1n = sbrow1[kn];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) xf[f] = frag(st.x[b], wm * 4 + f, fo0, fo1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wf[j] = frag(st.w0[b], wn * 4 + j, fo0, fo1);
+    vm_wait<16>();  // W1 of block kb landed (before phase 4kb+1 ends for either group)
+    barrier();
+    // C0
+    float sc0[4], sc1[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      sc0[f] = sac[f] * sb0c;
+      sc1[f] = kOne ? sc0[f] : sac[f] * sb1c;
+    }
+    cphase(0, 4, sc0, sc1);
+    barrier();
+    // M1
+    vm_order();
+    copy_xw0(kb + 2, buf);
+    vm_order();
+#pragma unroll
+    for (int j = 0; j < kNC1; ++j) wf[j] = frag(st.w1[b], wn * 4 + j, fo0, fo1);
+    vm_wait<12>();  // X/W0 of block kb + 1 landed
+    barrier();
+    // C1
+    cphase(4, kNC1, sc0, sc1);
+    barrier();
+  };
+
+  int kb = 0;
+  for (; kb + 1 < KB; kb += 2) {
+    kstep(kb, B0{}, saA, saB, sb0A, sb1A, sb0B, sb1B);
+    kstep(kb + 1, B1{}, saB, saA, sb0B, sb1B, sb0A, sb1A);
+  }
+  if (kb < KB) kstep(kb, B0{}, saA, saB, sb0A, sb1A, sb0B, sb1B);
+  if (lead) barrier();  // matches the lagging waves' extra first phase
+  vm_wait<0>();         // the copies past the last block (empty) and the scale loads
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[f][NFR - 1][i] = __builtin_fmaf(pp[f][i], sclp[f], acc[f][NFR - 1][i]);
+
+  // Epilogue (as gemm_tile): lane owns row m = m_begin + wm*64 + f*16 + l16 and columns
+  // wc0 + j*16 + 4*kg + {0..3}.
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const int r = wm * 64 + f * 16 + l16;
+    if (r >= t.rows) continue;
+    const int64_t m = t.m_begin + r;
+#pragma unroll
+    for (int j = 0; j < NFR; ++j) {
+      const int64_t n = wc0 + j * 16 + 4 * kg;
+      if (n >= t.n_end) continue;
+      const v4f v = acc[f][j];
+      if (out_f32) {
+        *reinterpret_cast<v4f *>(static_cast<float *>(c) + m * N + n) = v;
+      } else {
+        uint32_t bb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t u = __float_as_uint(v[i]);
+          bb[i] = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;  // round to nearest even
+        }
+        uint2 pk;
+        pk.x = bb[0] | (bb[1] << 16);
+        pk.y = bb[2] | (bb[3] << 16);
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(c) + m * N + n) = pk;
+      }
+    }
+  }
+}
+
+// Dense problem in 256 x (32*NFR) tiles with the ping-pong schedule, persistent like
+// gemm_blockscaled_split_kernel (workgroup b takes tiles b, b + gridDim.x, ...).
+template <int NFR>
+__global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(const uint8_t *__restrict__ xq,
+                                                              const float *__restrict__ sa,
+                                                              const uint8_t *__restrict__ wq,
+                                                              const float *__restrict__ sb, int64_t M, int64_t N,
+                                                              int64_t K, int total, void *__restrict__ c,
+                                                              int out_f32) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sx0[256 * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t sx1[256 * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t sw00[128 * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t sw01[128 * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t sw10[128 * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t sw11[128 * kBK];
+  const PPStages st = {{(FP8Q_LDS uint8_t *)sx0, (FP8Q_LDS uint8_t *)sx1},
+                       {(FP8Q_LDS uint8_t *)sw00, (FP8Q_LDS uint8_t *)sw01},
+                       {(FP8Q_LDS uint8_t *)sw10, (FP8Q_LDS uint8_t *)sw11}};
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    Tile t;
+    dense_tile<32 * NFR>(item, M, 0, N, wq, sb, t);
+    t.x = xq;
+    gemm_tile_pp<NFR, NFR == 8>(t, sa, M, N, K, c, out_f32, st);
+    __builtin_amdgcn_s_barrier();
+  }
+}
+
 #define FP8Q_DECLARE_STAGES(st, scale_bytes)                             \
   __shared__ __attribute__((aligned(1024))) uint8_t sx0[kBM * kBK];      \
   __shared__ __attribute__((aligned(1024))) uint8_t sw0[kBM * kBK];      \
@@ -611,9 +920,7 @@ hipError_t check_grouped_offsets(const int32_t *offsets, int64_t G, int64_t M_to
   return hipSuccess;
 }
 
-namespace {
-
-int device_cus() {
+int device_cu_count() {
   static int cus[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -624,6 +931,8 @@ int device_cus() {
   }
   return cus[dev];
 }
+
+namespace {
 
 #ifndef FP8Q_NARROW_COST
 #define FP8Q_NARROW_COST 0.82
@@ -692,10 +1001,46 @@ Plan dense_plan(int64_t M, int64_t N, int64_t cus) {
   return {tm * best_a, tm * ((N - best_a * 256 + 191) / 192), best_a * 256};
 }
 
+#ifndef FP8Q_PP
+#define FP8Q_PP 0
+#endif
+
+// Whether a dense problem runs on the ping-pong kernel: FP8Q_PP by default, overridden by
+// the environment variable FP8Q_DENSE_KERNEL ("pp" or "split"); the kernel's 32-bit buffer
+// offsets need M * K/128 < 2^30.
+bool use_pp(int64_t M, int64_t K) {
+  bool pp = FP8Q_PP != 0;
+  const char *e = getenv("FP8Q_DENSE_KERNEL");
+  if (e && strcmp(e, "pp") == 0) pp = true;
+  if (e && strcmp(e, "split") == 0) pp = false;
+  return pp && M * (K / 128) < (static_cast<int64_t>(1) << 30);
+}
+
 template <bool kRowB>
 hipError_t launch_dense(const uint8_t *xq, const float *sa, const uint8_t *wq, const float *sb, int64_t M,
                         int64_t N, int64_t K, void *c, bool out_f32, hipStream_t stream) {
-  const int64_t cus = device_cus();
+  const int64_t cus = device_cu_count();
+  if (!kRowB && use_pp(M, K)) {
+    // 256- or 224-wide tiles, whichever finishes first when every CU takes tiles in rounds
+    // (a 224-wide tile costs 7/8 of a 256-wide one); FP8Q_PP_WIDTH=256|224 forces one.
+    const int64_t tm = (M + kBM - 1) / kBM;
+    const int64_t t256 = tm * ((N + 255) / 256), t224 = tm * ((N + 223) / 224);
+    const int64_t slots = (cus / 8) * 8 > 0 ? (cus / 8) * 8 : cus;
+    bool narrow = ((t224 + slots - 1) / slots) * 7 < ((t256 + slots - 1) / slots) * 8;
+    const char *wforce = getenv("FP8Q_PP_WIDTH");
+    if (wforce && strcmp(wforce, "256") == 0) narrow = false;
+    if (wforce && strcmp(wforce, "224") == 0) narrow = true;
+    const int64_t tiles = narrow ? t224 : t256;
+    if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+    const int64_t grid = min(tiles, slots);
+    if (narrow)
+      hipLaunchKernelGGL(gemm_pp_kernel<7>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream, xq, sa, wq,
+                         sb, M, N, K, static_cast<int>(tiles), c, out_f32 ? 1 : 0);
+    else
+      hipLaunchKernelGGL(gemm_pp_kernel<8>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream, xq, sa, wq,
+                         sb, M, N, K, static_cast<int>(tiles), c, out_f32 ? 1 : 0);
+    return hipGetLastError();
+  }
   const int64_t tm = (M + kBM - 1) / kBM;
   if (tm * ((N + 191) / 192) > 0x7fffffff) return hipErrorInvalidValue;
   const Plan p = dense_plan(M, N, cus);

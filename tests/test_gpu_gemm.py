@@ -7,7 +7,8 @@ spanning several 256x256 tiles with partial tails in M and N, an exactly represe
 integer case (bit-exact, pins the MFMA operand and output layouts), a characterisation of
 the matrix core's own block summation, the dense 4096x7168x7168
 workload in the benchmarked launch (every output), grouped MoE shapes with
-empty / 1 / 127..257-row experts, the MoE up/down workloads (sampled experts), run-to-run
+empty / 1 / 127..257-row experts and with 65..256 experts (several offset-scan chunks), the
+MoE up/down workloads (every expert on sampled column blocks; four experts in full), run-to-run
 determinism, the dense tile plans (uniform 256-wide tiles or a 256/192-wide column split,
 bit-identical to each other) and untouched rows outside every expert range."""
 import numpy as np
@@ -129,6 +130,30 @@ def test_dense_tile_plans(M, N, K, monkeypatch):
         assert np.array_equal(outs[plan], outs["off"]), plan
 
 
+@pytest.mark.parametrize("width", ["256", "224"])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (300, 1152, 1024), (257, 640, 384), (40, 128, 256),
+                                   (513, 768, 2176), (1024, 1024, 7168), (260, 2688, 512)])
+def test_dense_pingpong_kernel(M, N, K, width, monkeypatch):
+    """The ping-pong kernel (256 x 256 or 256 x 224 tiles, the two waves of a SIMD
+    alternating between LDS reads and MFMAs) against the oracle bound, and bit-identical to
+    the column-split kernel: the same block partials folded in the same order.  224-wide
+    tiles put wave columns across 128-column weight-scale blocks (N = 2688 = 12 x 224)."""
+    xq, sa, wq, sb = quantized(M, N, K, seed=11 * M + N + K, xscale=2.0)
+    ref = og.gemm_blockscaled(xq, sa, wq, sb)
+    xn, wn = og.row_norms_act(xq, sa), og.row_norms_w(wq, sb)
+    monkeypatch.setenv("FP8Q_PP_WIDTH", width)
+    monkeypatch.setenv("FP8Q_DENSE_KERNEL", "pp")
+    pp32 = gpu_gemm(xq, sa, wq, sb, torch.float32)
+    ppbf = gpu_gemm(xq, sa, wq, sb)
+    monkeypatch.setenv("FP8Q_DENSE_KERNEL", "split")
+    sp32 = gpu_gemm(xq, sa, wq, sb, torch.float32)
+    spbf = gpu_gemm(xq, sa, wq, sb)
+    assert_gemm_within_tol(pp32, ref, xn, wn, f"pp {M}x{N}x{K} f32")
+    assert_gemm_within_tol(ppbf, ref, xn, wn, f"pp {M}x{N}x{K} bf16")
+    assert np.array_equal(pp32, sp32)
+    assert np.array_equal(ppbf, spbf)
+
+
 def test_deterministic():
     xq, sa, wq, sb = quantized(300, 640, 512, seed=5)
     a = fq.fp8q_gemm_blockscaled(dev(xq), dev(sa), dev(wq), dev(sb))
@@ -207,6 +232,44 @@ def test_grouped_edge_sizes(sizes):
             assert_gemm_within_tol(got[lo:hi], ref[lo:hi], xn[lo:hi], wn, f"expert {g} ({hi - lo} rows)")
 
 
+def _grouped_sizes(G, seed, zero=(), fixed=None):
+    rng = np.random.default_rng(seed)
+    sizes = rng.integers(0, 48, size=G)
+    sizes[list(zero)] = 0
+    for g, n in (fixed or {}).items():
+        sizes[g] = n
+    return sizes
+
+
+@pytest.mark.parametrize("G,zero,fixed", [
+    # one expert past the first 64-expert chunk; the last expert of the first chunk empty
+    (65, (63,), {64: 130, 0: 257}),
+    # empty experts on both sides of the chunk boundary, ragged tails <= 128 and > 128 rows
+    (128, (62, 63, 64, 65), {66: 100, 127: 257, 1: 129}),
+    # four chunks, empty experts around every boundary, the very last expert non-empty
+    (256, (63, 64, 127, 128, 191, 192), {193: 1, 255: 129, 100: 300, 200: 128}),
+    # all experts of the first chunk empty: every row lives in later chunks
+    (130, tuple(range(64)), {64: 200, 129: 5}),
+])
+def test_grouped_many_experts(G, zero, fixed):
+    """More experts than one scan chunk (the kernel scans the offsets 64 experts at a
+    time): experts found in later chunks, empty experts at chunk edges, ragged tails."""
+    sizes = _grouped_sizes(G, seed=G, zero=zero, fixed=fixed)
+    offsets = np.zeros(G + 1, np.int32)
+    offsets[1:] = np.cumsum(sizes)
+    M, N, K = int(offsets[-1]), 256, 256
+    xq, sa, wq, sb = quantized(M, N, K, seed=G + 1, G=G, xscale=2.0)
+    ref = og.grouped_gemm_blockscaled(xq, sa, wq, sb, offsets)
+    got = run_grouped(xq, sa, wq, sb, offsets, out_dtype=torch.float32, fill=-777.0)
+    xn = og.row_norms_act(xq, sa)
+    for g in range(G):
+        lo, hi = int(offsets[g]), int(offsets[g + 1])
+        if hi > lo:
+            assert_gemm_within_tol(got[lo:hi], ref[lo:hi], xn[lo:hi], og.row_norms_w(wq[g], sb[g]),
+                                   f"G={G} expert {g} ({hi - lo} rows)")
+    assert not np.any(got == -777.0)
+
+
 def test_grouped_single_expert_equals_dense():
     xq, sa, wq, sb = quantized(300, 640, 384, seed=21)
     dense = gpu_gemm(xq, sa, wq, sb)
@@ -248,6 +311,44 @@ def test_grouped_debug_offsets_check(monkeypatch):
         assert bool(torch.all(out == -5.0)), bad
     monkeypatch.setenv("FP8Q_DEBUG", "0")
     run_grouped(xq, sa, wq, sb, np.array([0, 130, 60, 200], np.int32))  # clamped, no check
+
+
+@pytest.mark.parametrize("name", ["moe_up", "moe_down"])
+def test_moe_workloads_all_experts(name):
+    """Full-size MoE workloads, every one of the 32 experts checked: all of its rows
+    against two 128-column blocks of its output (a different pair per expert, so the
+    experts together cover every column block and both tile shapes' positions).  The GPU
+    quantizes everything; the rows of X and the sampled weight blocks are also quantized by
+    the oracle, must equal the GPU's codes bit for bit, and are what the reference uses."""
+    c = wl.CONFIGS[name]()
+    offsets = c["offsets"]
+    x_d = dev_bf16(c["x"])
+    w_d = dev_bf16(c["w"])
+    xq_d, sa_d = fq.fp8q_quantize_act_1x128(x_d)
+    wq_d, sb_d = fq.fp8q_quantize_w_128x128(w_d)
+    out = fq.fp8q_grouped_gemm_blockscaled(xq_d, sa_d, wq_d, sb_d, dev(offsets))
+    torch.cuda.synchronize()
+    got = host(out).astype(np.float64)
+    xq, sa = oq.quantize_act_1x128(c["x"])
+    assert_quant_equal(xq_d, sa_d, xq, sa, f"{name} activations")
+    G, N, K = c["w"].shape
+    NB = N // 128
+    xh = oq.dequant_act(xq, sa)
+    checked = 0
+    for g in range(G):
+        lo, hi = int(offsets[g]), int(offsets[g + 1])
+        for nb in sorted({g % NB, (7 * g + NB // 2 + 3) % NB}):
+            wq_b, sb_b = oq.quantize_w_128x128(c["w"][g, nb * 128:(nb + 1) * 128])
+            assert_quant_equal(wq_d[g, nb * 128:(nb + 1) * 128], sb_d[g, nb:nb + 1], wq_b, sb_b,
+                               f"{name} expert {g} weight block row {nb}")
+            if hi == lo:
+                continue
+            wh = oq.dequant_w(wq_b, sb_b)
+            assert_gemm_within_tol(got[lo:hi, nb * 128:(nb + 1) * 128], xh[lo:hi] @ wh.T,
+                                   np.linalg.norm(xh[lo:hi], axis=1), np.linalg.norm(wh, axis=1),
+                                   f"{name} expert {g} cols {nb * 128}..{nb * 128 + 127}")
+            checked += hi - lo
+    assert checked >= int(offsets[-1])
 
 
 @pytest.mark.parametrize("name", ["moe_up", "moe_down"])
