@@ -222,16 +222,21 @@ __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict
   const int jsplit = static_cast<int>((128 - (wc0 & 127)) >> 4);
   const float *sbrow0 = t.sb + static_cast<int64_t>(kRowB ? 0 : nb0) * KB;
   const float *sbrow1 = t.sb + static_cast<int64_t>(kRowB ? 0 : nb1) * KB;
-  // Row-scaled B: the stage's column scales (lane l copies columns 4l .. 4l+3 of the
-  // tile).  Every wave issues the same 1 KB copy to the same LDS words: the writes are
-  // identical, and a branch here would split the loop body.  The buffer's range check
-  // counts the block's row offset (the scalar offset) too, so the resource spans the rest
-  // of the scale matrix; the copies past the tile's last column read other columns'
-  // finite scales, which only ever meet zero partials.
-  const __amdgpu_buffer_rsrc_t rsc = make_rsrc(t.sb + t.n0, static_cast<uint32_t>((KB * N - t.n0) * 4));
+  // Row-scaled B: the stage's 256 column scales (1 KB).  Waves 0-3 each copy a quarter
+  // (4 bytes per lane, columns 64q .. 64q+63 to bytes 256q ..), waves 4-7 issue the same
+  // copy through an empty resource (zeros, no memory traffic) into the unread second KB of
+  // the 2 KB stage array: every wave issues one copy per stage (no branch in the loop body)
+  // and the scales cross the fabric once.  The buffer's range check counts the block's row
+  // offset (the scalar offset) too, so the resource spans the rest of the scale matrix; the
+  // copies past the tile's last column read other columns' finite scales, which only ever
+  // meet zero partials.
+  const int sq = wave & 3;
+  const __amdgpu_buffer_rsrc_t rsc =
+      wave < 4 ? make_rsrc(t.sb + t.n0, static_cast<uint32_t>((KB * N - t.n0) * 4)) : make_rsrc(t.sb, 0u);
+  const int sc_dst = (wave < 4 ? 0 : 1024) + sq * 256;
   auto scale_load = [&](int kb, FP8Q_LDS uint8_t *dst) {
     if (kRowB)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, (FP8Q_LDS void *)dst, 16, lane * 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, (FP8Q_LDS void *)(dst + sc_dst), 4, sq * 256 + lane * 4,
                                                static_cast<int>(kb * N * 4), 0, 0);
   };
 
@@ -430,8 +435,9 @@ __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict
 // its last read and its next copy (two K blocks ahead) gets about one and a half K blocks
 // of time to land: the copies of X and W0 for block kb + 2 are issued in M1(kb), those of
 // W1 for block kb + 1 in M0(kb), with the activation scales of block kb + 1.  Per K block a
-// wave issues 6 + 2 + 4 vector memory operations in that order, so fixed vmcnt counts name
-// exactly the copies that must have landed before the barrier preceding their first read.
+// wave issues a fixed number of vector memory operations in a fixed order (with the 4 x 2
+// wave grid: 6 copies of X/W0, 2 of W1, 4 scale loads), so fixed vmcnt counts name exactly
+// the copies that must have landed before the barrier preceding their first read.
 // Copies past the last K block read through an empty buffer resource (zeros, no memory
 // traffic) and keep the counts uniform.  Every wave waits for its own copies at the end of
 // its M phases (the loop body has no branch: a branch there lets the compiler move the
@@ -455,26 +461,30 @@ __device__ __forceinline__ void vm_wait() {
 // wave's columns lie in one 128-column weight-scale block (256-wide tiles starting at a
 // multiple of 256), so a fragment row has one promotion scale per K block; otherwise each
 // fragment column picks the scale of its block.
-template <int NFR, bool kOne>
+template <int WM, int NFR, bool kOne>
 __device__ __forceinline__ void gemm_tile_pp(const Tile &t, const float *__restrict__ sa, int64_t M, int64_t N,
                                              int64_t K, void *__restrict__ c, int out_f32, const PPStages &st) {
-  static_assert(NFR == 7 || NFR == 8, "tile width 224 or 256");
+  static_assert(NFR == 7 || NFR == 8, "wave columns 112 or 128");
+  static_assert(WM == 4 || (WM == 2 && NFR == 8), "wave grid 4 x 2, or 2 x 4 with 128-column waves");
   static_assert(!kOne || NFR == 8, "one scale block per wave needs 128-column waves");
+  constexpr int WN = 8 / WM;     // wave columns
   constexpr int kWN = 16 * NFR;  // columns per wave
   constexpr int kNC1 = NFR - 4;  // fragment columns of C1
+  // vector memory operations per K block: X/W0 copies, W1 copies, activation scales
+  constexpr int kXW0 = WM + WN, kW1 = WN, kSA = 4;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool lead = wave < 4;  // waves 0-3 run one phase ahead
-  const int wm = wave >> 1;    // rows wm*64 .. +63
-  const int wn = wave & 1;     // cols wn*kWN .. +kWN-1
+  const int wm = wave / WN;    // rows wm*64 .. +63
+  const int wn = wave % WN;    // cols wn*kWN .. +kWN-1
   const int KB = static_cast<int>(K >> 7);
   const int NB = static_cast<int>(N >> 7);
   const int l16 = lane & 15;
   const int kg = lane >> 4;
 
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(t.x + t.m_begin * K, static_cast<uint32_t>(t.rows * K));
-  const int rows_w = static_cast<int>(min(static_cast<int64_t>(2 * kWN), t.n_end - t.n0));
+  const int rows_w = static_cast<int>(min(static_cast<int64_t>(WN * kWN), t.n_end - t.n0));
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(t.w + t.n0 * K, static_cast<uint32_t>(rows_w * K));
   const __amdgpu_buffer_rsrc_t rnull = make_rsrc(t.x, 0u);
   // Activation scales of the tile's rows: sa[kb][m_begin + r] at byte kb*M*4 + r*4; rows
@@ -483,8 +493,10 @@ __device__ __forceinline__ void gemm_tile_pp(const Tile &t, const float *__restr
 
   // Copies: every 1 KB block this wave moves lands on rows rowbase + 16*(block/2) of its
   // region (the stage layout of lds_pos), so one per-lane offset serves all of them; the
-  // rest is a scalar offset.  X: blocks 8i + wave, tile rows 64i + rowbase.  Weight region
-  // r: blocks 8i + wave, tile rows kWN*i + 64r + rowbase (region group 4i + wave/2).
+  // rest is a scalar offset.  X (64*WM rows): blocks 8i + wave, i < WM, tile rows
+  // 64i + rowbase.  Weight region r (64 rows of each of the WN wave columns): blocks
+  // 8i + wave, i < WN, region group 4i + wave/2 = rows 16*(wave/2) .. of wave column i,
+  // tile rows kWN*i + 64r + rowbase.
   const int line = 4 * (wave & 1) + (lane >> 4);
   const int rowbase = 16 * (wave >> 1) + line + 8 * ((lane >> 3) & 1);
   const int voff = rowbase * static_cast<int>(K) + (((lane & 7) ^ line) << 4);
@@ -516,11 +528,11 @@ __device__ __forceinline__ void gemm_tile_pp(const Tile &t, const float *__restr
     const __amdgpu_buffer_rsrc_t r_x = ok ? rx : rnull, r_w = ok ? rw : rnull;
     const int koff = ok ? s * kBK : 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WM; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r_x, (FP8Q_LDS void *)(st.x[b] + (8 * i + wave) * 1024), 16, voff,
                                                koff + 64 * i * K32, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < WN; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r_w, (FP8Q_LDS void *)(st.w0[b] + (8 * i + wave) * 1024), 16, voff,
                                                koff + kWN * i * K32, 0, 0);
   };
@@ -530,7 +542,7 @@ __device__ __forceinline__ void gemm_tile_pp(const Tile &t, const float *__restr
     const __amdgpu_buffer_rsrc_t r_w = ok ? rw : rnull;
     const int koff = ok ? s * kBK : 0;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < WN; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r_w, (FP8Q_LDS void *)(st.w1[b] + (8 * i + wave) * 1024), 16, voff,
                                                koff + (kWN * i + 64) * K32, 0, 0);
   };
@@ -576,7 +588,7 @@ __device__ __forceinline__ void gemm_tile_pp(const Tile &t, const float *__restr
   load_sa(0, saA);
   vm_order();
   copy_xw0(1, B1{});
-  vm_wait<12>();  // X/W0 of block 0 landed (W1 0, the scales and X/W0 1 may be in flight)
+  vm_wait<kW1 + kSA + kXW0>();  // X/W0 of block 0 landed (W1 0, the scales, X/W0 1 may be in flight)
   barrier();
   if (!lead) barrier();  // the lagging waves' first phase is idle
 
@@ -613,7 +625,13 @@ __device__ __forceinline__ void gemm_tile_pp(const Tile &t, const float *__restr
                    float &sb1n) {
     constexpr int b = decltype(buf)::value;
     using Next = std::integral_constant<int, 1 - b>;
-    // M0
+    // M0: the fragment reads first (ahead of this phase's copies), then the copies of W1
+    // for block kb + 1 and the scales of block kb + 1; this block's promotion scales are
+    // formed before the barrier so that C0 starts with its first MFMA.
+#pragma unroll
+    for (int f = 0; f < 4; ++f) xf[f] = frag(st.x[b], wm * 4 + f, fo0, fo1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wf[j] = frag(st.w0[b], wn * 4 + j, fo0, fo1);
     vm_order();
     copy_w1(kb + 1, Next{});
     vm_order();
@@ -622,28 +640,27 @@ __device__ __forceinline__ void gemm_tile_pp(const Tile &t, const float *__restr
     const int kn = kb + 1 < KB ? kb + 1 : KB - 1;
     sb0n = sbrow0[kn];
     if (!kOne) sb1n = sbrow1[kn];
-#pragma unroll
-    for (int f = 0; f < 4; ++f) xf[f] = frag(st.x[b], wm * 4 + f, fo0, fo1);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) wf[j] = frag(st.w0[b], wn * 4 + j, fo0, fo1);
-    vm_wait<16>();  // W1 of block kb landed (before phase 4kb+1 ends for either group)
-    barrier();
-    // C0
+    // W1 of block kb landed (before phase 4kb+1 ends for either group); issued after it:
+    // the scales of kb, X/W0 of kb+1, W1 and the scales of kb+1
+    vm_wait<kSA + kXW0 + kW1 + kSA>();
     float sc0[4], sc1[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       sc0[f] = sac[f] * sb0c;
       sc1[f] = kOne ? sc0[f] : sac[f] * sb1c;
     }
+    barrier();
+    // C0
     cphase(0, 4, sc0, sc1);
     barrier();
     // M1
+#pragma unroll
+    for (int j = 0; j < kNC1; ++j) wf[j] = frag(st.w1[b], wn * 4 + j, fo0, fo1);
     vm_order();
     copy_xw0(kb + 2, buf);
     vm_order();
-#pragma unroll
-    for (int j = 0; j < kNC1; ++j) wf[j] = frag(st.w1[b], wn * 4 + j, fo0, fo1);
-    vm_wait<12>();  // X/W0 of block kb + 1 landed
+    // X/W0 of block kb + 1 landed; issued after it: W1 and the scales of kb+1, X/W0 of kb+2
+    vm_wait<kW1 + kSA + kXW0>();
     barrier();
     // C1
     cphase(4, kNC1, sc0, sc1);
@@ -715,7 +732,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(const uint8_t *__r
     Tile t;
     dense_tile<32 * NFR>(item, M, 0, N, wq, sb, t);
     t.x = xq;
-    gemm_tile_pp<NFR, NFR == 8>(t, sa, M, N, K, c, out_f32, st);
+    gemm_tile_pp<4, NFR, NFR == 8>(t, sa, M, N, K, c, out_f32, st);
     __builtin_amdgcn_s_barrier();
   }
 }
@@ -749,7 +766,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_split_kernel(
     const uint8_t *__restrict__ xq, const float *__restrict__ sa, const uint8_t *__restrict__ wq,
     const float *__restrict__ sb, int64_t M, int64_t N, int64_t K, int64_t n_split, int tiles1, int total,
     void *__restrict__ c, int out_f32) {
-  FP8Q_DECLARE_STAGES(st, kRowB ? 1024 : 16);
+  FP8Q_DECLARE_STAGES(st, kRowB ? 2048 : 16);
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     Tile t;
     if (item < tiles1) {
@@ -861,27 +878,33 @@ __device__ __forceinline__ int grouped_item(const int32_t *__restrict__ offsets,
   return -1;
 }
 
-// Grouped GEMM with both tile shapes in one launch; the two 80 KB LDS halves hold one stage
-// each (activation rows first, then weight rows), which fits either shape.
+// Grouped GEMM with both tile shapes in one launch, each on the ping-pong schedule: 256 x 256
+// items with the 4 x 2 wave grid, 128 x 512 items with 2 x 4.  Six LDS arrays (32 + 32 +
+// 16 + 16 + 32 + 32 KB) hold either layout: X in A and W0 in B for 256 x 256 (32 + 16 KB
+// per stage), X in B and W0 in A for 128 x 512 (16 + 32 KB), W1 in C for both.
 __global__ __launch_bounds__(kThreads, 1) void gemm_grouped_kernel(
     const uint8_t *__restrict__ xq, const float *__restrict__ sa, const uint8_t *__restrict__ wq,
     const float *__restrict__ sb, const int32_t *__restrict__ offsets, int G, int64_t M, int64_t N,
     int64_t K, void *__restrict__ c, int out_f32) {
-  constexpr int kHalf = 80 * 1024;
-  __shared__ __attribute__((aligned(1024))) uint8_t sbuf0[kHalf];
-  __shared__ __attribute__((aligned(1024))) uint8_t sbuf1[kHalf];
-  FP8Q_LDS uint8_t *b0 = (FP8Q_LDS uint8_t *)sbuf0;
-  FP8Q_LDS uint8_t *b1 = (FP8Q_LDS uint8_t *)sbuf1;
+  __shared__ __attribute__((aligned(1024))) uint8_t sa0[32768];
+  __shared__ __attribute__((aligned(1024))) uint8_t sa1[32768];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb0[16384];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb1[16384];
+  __shared__ __attribute__((aligned(1024))) uint8_t sc0[32768];
+  __shared__ __attribute__((aligned(1024))) uint8_t sc1[32768];
+  FP8Q_LDS uint8_t *A0 = (FP8Q_LDS uint8_t *)sa0, *A1 = (FP8Q_LDS uint8_t *)sa1;
+  FP8Q_LDS uint8_t *B0 = (FP8Q_LDS uint8_t *)sb0, *B1 = (FP8Q_LDS uint8_t *)sb1;
+  FP8Q_LDS uint8_t *C0 = (FP8Q_LDS uint8_t *)sc0, *C1 = (FP8Q_LDS uint8_t *)sc1;
   Tile t;
   const int shape = grouped_item(offsets, G, M, N, K, wq, sb, t);
   if (shape < 0) return;
   t.x = xq;
   if (shape == 0) {
-    const Stages st = {b0, b0 + 256 * kBK, b1, b1 + 256 * kBK, nullptr, nullptr};
-    gemm_tile<8, false, 4>(t, sa, M, N, K, c, out_f32, st);
+    const PPStages st = {{A0, A1}, {B0, B1}, {C0, C1}};
+    gemm_tile_pp<4, 8, true>(t, sa, M, N, K, c, out_f32, st);
   } else {
-    const Stages st = {b0, b0 + 128 * kBK, b1, b1 + 128 * kBK, nullptr, nullptr};
-    gemm_tile<8, false, 2>(t, sa, M, N, K, c, out_f32, st);
+    const PPStages st = {{B0, B1}, {A0, A1}, {C0, C1}};
+    gemm_tile_pp<2, 8, true>(t, sa, M, N, K, c, out_f32, st);
   }
 }
 
@@ -1002,7 +1025,7 @@ Plan dense_plan(int64_t M, int64_t N, int64_t cus) {
 }
 
 #ifndef FP8Q_PP
-#define FP8Q_PP 0
+#define FP8Q_PP 1
 #endif
 
 // Whether a dense problem runs on the ping-pong kernel: FP8Q_PP by default, overridden by
@@ -1021,12 +1044,14 @@ hipError_t launch_dense(const uint8_t *xq, const float *sa, const uint8_t *wq, c
                         int64_t N, int64_t K, void *c, bool out_f32, hipStream_t stream) {
   const int64_t cus = device_cu_count();
   if (!kRowB && use_pp(M, K)) {
-    // 256- or 224-wide tiles, whichever finishes first when every CU takes tiles in rounds
-    // (a 224-wide tile costs 7/8 of a 256-wide one); FP8Q_PP_WIDTH=256|224 forces one.
+    // 256-wide tiles, or 224-wide ones when that takes fewer rounds of tiles over the CUs:
+    // a 224-wide tile measures about as long as a 256-wide one (its waves' columns straddle
+    // weight-scale blocks, one select per promoted fragment), so it only pays when it saves
+    // whole rounds.  FP8Q_PP_WIDTH=256|224 forces one.
     const int64_t tm = (M + kBM - 1) / kBM;
     const int64_t t256 = tm * ((N + 255) / 256), t224 = tm * ((N + 223) / 224);
     const int64_t slots = (cus / 8) * 8 > 0 ? (cus / 8) * 8 : cus;
-    bool narrow = ((t224 + slots - 1) / slots) * 7 < ((t256 + slots - 1) / slots) * 8;
+    bool narrow = (t224 + slots - 1) / slots < (t256 + slots - 1) / slots;
     const char *wforce = getenv("FP8Q_PP_WIDTH");
     if (wforce && strcmp(wforce, "256") == 0) narrow = false;
     if (wforce && strcmp(wforce, "224") == 0) narrow = true;
