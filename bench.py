@@ -129,6 +129,15 @@ def measured_traffic(workload: str):
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemm_counters.json")
 
 
+def dense_kernel_name():
+    """The dense GEMM kernel the library launches for the benchmarked shapes: the ping-pong
+    kernel (256-wide tiles for every shape here), or the split-plan kernel when
+    FP8Q_DENSE_KERNEL=split selects it."""
+    if os.environ.get("FP8Q_DENSE_KERNEL", "") == "split":
+        return "gemm_blockscaled_split_kernel<8, 6, false>"
+    return "gemm_pp_kernel<8>"
+
+
 def measured_counters(kernel_substring: str):
     """Matrix-core busy, vector-ALU busy and LDS figures of the GEMM from the committed
     counter summary (fp8_fine_grained_fp8q_amd/counter_summary.py), only if it was taken on
@@ -728,18 +737,25 @@ def main():
     a_act, a_w, a_g = (per[0] * 1e-6, 0.0, per[1] * 1e-6) if fused else (per[0] * 1e-6, per[1] * 1e-6, per[2] * 1e-6)
     gemm_tflops = flops / a_g / 1e12
     traffic = measured_traffic(args.workload)
-    roofline = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
-                "kernel": "gemm_grouped_kernel" if grouped else "gemm_blockscaled_split_kernel<8, 6, false>",
-                "flop_per_launch": flops, "avg_launch_us": round(a_g * 1e6, 2),
-                "algorithmic_bytes_per_launch": bytes_gemm}
-    counters = measured_counters("gemm_grouped_kernel" if grouped else "gemm_")
+    hbm_gbs = bytes_gemm / a_g / 1e9
+    # the binding roof is the one whose time at peak is longer: MFMA for the dense shapes,
+    # HBM for the expert GEMMs (each expert's weights are read for a few hundred rows)
+    hbm_bound = bytes_gemm / (PEAK_HBM_GBS * 1e9) > flops / (PEAK_FP8_TFLOPS * 1e12)
+    kernel = "gemm_grouped_kernel" if grouped else dense_kernel_name()
+    if hbm_bound:
+        roofline = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(hbm_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                    "mfma_achieved_TFLOPs": round(gemm_tflops, 1),
+                    "mfma_frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4)}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
+                    "hbm_achieved_GBs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4)}
+    roofline.update({"kernel": kernel, "flop_per_launch": flops, "avg_launch_us": round(a_g * 1e6, 2),
+                     "algorithmic_bytes_per_launch": bytes_gemm})
+    counters = measured_counters("gemm_grouped_kernel" if grouped else "gemm_pp")
     if counters:
         roofline["counters"] = counters
-    if grouped:
-        # the expert-weight stream bounds the grouped GEMM: report the HBM view as well
-        roofline["hbm_achieved_GBs"] = round(bytes_gemm / a_g / 1e9, 1)
-        roofline["hbm_frac"] = round(bytes_gemm / a_g / 1e9 / PEAK_HBM_GBS, 4)
 
     line = {
         "metric": METRIC,

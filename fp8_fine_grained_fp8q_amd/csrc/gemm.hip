@@ -423,12 +423,13 @@ __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict
 // waves 0-3 run one phase ahead of the waves 4-7, so in every phase each SIMD has one wave
 // feeding its matrix core and the LDS reads never sit between a barrier and the first MFMA.
 //
-// Each wave owns 64 rows x 128 columns as before.  A K block is four phases for a wave:
-//   M0: read the activation fragments (4 row groups) and the weight fragments of its
+// Each wave owns 16*FM rows (FM = 4 for full 256-row tiles; the grouped kernel also runs
+// 64-, 128- and 192-row tiles) x 128 columns.  A K block is four phases for a wave:
+//   M0: read the activation fragments (FM row groups) and the weight fragments of its
 //       column half 0 (fragment columns 0-3),
-//   C0: 16 MFMAs (4 x 4 fragments) with the promotion FMAs in their shadow,
+//   C0: 4*FM MFMAs (FM x 4 fragments) with the promotion FMAs in their shadow,
 //   M1: read the weight fragments of column half 1 (fragment columns 4-7),
-//   C1: 16 MFMAs and promotion.
+//   C1: 4*FM MFMAs and promotion.
 // The LDS stage is split into three regions: X (activation rows), W0 (the weight rows of
 // column half 0 of both wave columns) and W1 (half 1).  X and W0 are read only in M0
 // phases and W1 only in M1 phases, so with two buffers each region is free two phases after
@@ -436,7 +437,7 @@ __device__ __forceinline__ void gemm_tile(const Tile &t, const float *__restrict
 // of time to land: the copies of X and W0 for block kb + 2 are issued in M1(kb), those of
 // W1 for block kb + 1 in M0(kb), with the activation scales of block kb + 1.  Per K block a
 // wave issues a fixed number of vector memory operations in a fixed order (with the 4 x 2
-// wave grid: 6 copies of X/W0, 2 of W1, 4 scale loads), so fixed vmcnt counts name exactly
+// wave grid: FM + 2 copies of X/W0, 2 of W1, FM scale loads), so fixed vmcnt counts name exactly
 // the copies that must have landed before the barrier preceding their first read.
 // Copies past the last K block read through an empty buffer resource (zeros, no memory
 // traffic) and keep the counts uniform.  Every wave waits for its own copies at the end of
@@ -454,29 +455,32 @@ __device__ __forceinline__ void vm_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Computes the 256 x (32 * NFR) tile t, NFR = 8 (256 wide) or 7 (224 wide): each wave owns
-// 64 rows x 16*NFR columns, C0 covers its fragment columns 0-3 and C1 columns 4 .. NFR-1.
+// Computes the (16 * WM * FM) x (32 * NFR) tile t, NFR = 8 (256 wide) or 7 (224 wide),
+// WM = 4 wave rows (or 2 with 4 wave columns), FM = 1..4: each wave owns 16*FM rows x 16*NFR
+// columns, C0 covers its fragment columns 0-3 and C1 columns 4 .. NFR-1.
 // The weight regions always hold 8 row groups; with NFR = 7 the last group of each wave
 // column in W1 is never read and its copies go through the empty resource.  kOne: every
 // wave's columns lie in one 128-column weight-scale block (256-wide tiles starting at a
 // multiple of 256), so a fragment row has one promotion scale per K block; otherwise each
 // fragment column picks the scale of its block.
-template <int WM, int NFR, bool kOne>
+template <int WM, int NFR, bool kOne, int FM = 4>
 __device__ __forceinline__ void gemm_tile_pp(const Tile &t, const float *__restrict__ sa, int64_t M, int64_t N,
                                              int64_t K, void *__restrict__ c, int out_f32, const PPStages &st) {
   static_assert(NFR == 7 || NFR == 8, "wave columns 112 or 128");
   static_assert(WM == 4 || (WM == 2 && NFR == 8), "wave grid 4 x 2, or 2 x 4 with 128-column waves");
   static_assert(!kOne || NFR == 8, "one scale block per wave needs 128-column waves");
+  static_assert(FM >= 1 && FM <= 4 && (WM * FM) % 4 == 0, "fragment rows per wave 1..4, whole X copies");
   constexpr int WN = 8 / WM;     // wave columns
   constexpr int kWN = 16 * NFR;  // columns per wave
   constexpr int kNC1 = NFR - 4;  // fragment columns of C1
   // vector memory operations per K block: X/W0 copies, W1 copies, activation scales
-  constexpr int kXW0 = WM + WN, kW1 = WN, kSA = 4;
+  constexpr int kXI = WM * FM / 4;  // X copies per wave (64*WM*FM/4 rows, 8 rows per copy and wave)
+  constexpr int kXW0 = kXI + WN, kW1 = WN, kSA = FM;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool lead = wave < 4;  // waves 0-3 run one phase ahead
-  const int wm = wave / WN;    // rows wm*64 .. +63
+  const int wm = wave / WN;    // rows wm*16*FM .. +16*FM-1
   const int wn = wave % WN;    // cols wn*kWN .. +kWN-1
   const int KB = static_cast<int>(K >> 7);
   const int NB = static_cast<int>(N >> 7);
@@ -502,7 +506,7 @@ __device__ __forceinline__ void gemm_tile_pp(const Tile &t, const float *__restr
   const int voff = rowbase * static_cast<int>(K) + (((lane & 7) ^ line) << 4);
   const bool w1_pad = (wave >> 1) >= kNC1;  // this wave's W1 blocks are the unused groups
   const int fo0 = lds_pos(l16, 2 * kg), fo1 = lds_pos(l16, 2 * kg + 1);
-  const int sa_off = (wm * 64 + l16) * 4;  // + f*64 for fragment row f
+  const int sa_off = (wm * 16 * FM + l16) * 4;  // + f*64 for fragment row f
 
   // Weight-block scales: the wave's columns start in block nb0; fragment columns
   // j >= jsplit lie in block nb0 + 1.
@@ -513,9 +517,9 @@ __device__ __forceinline__ void gemm_tile_pp(const Tile &t, const float *__restr
   const float *sbrow0 = t.sb + static_cast<int64_t>(nb0) * KB;
   const float *sbrow1 = t.sb + static_cast<int64_t>(nb1) * KB;
 
-  v4f acc[4][NFR];
+  v4f acc[FM][NFR];
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
+  for (int f = 0; f < FM; ++f)
 #pragma unroll
     for (int j = 0; j < NFR; ++j) acc[f][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
@@ -528,7 +532,7 @@ __device__ __forceinline__ void gemm_tile_pp(const Tile &t, const float *__restr
     const __amdgpu_buffer_rsrc_t r_x = ok ? rx : rnull, r_w = ok ? rw : rnull;
     const int koff = ok ? s * kBK : 0;
 #pragma unroll
-    for (int i = 0; i < WM; ++i)
+    for (int i = 0; i < kXI; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r_x, (FP8Q_LDS void *)(st.x[b] + (8 * i + wave) * 1024), 16, voff,
                                                koff + 64 * i * K32, 0, 0);
 #pragma unroll
@@ -546,10 +550,10 @@ __device__ __forceinline__ void gemm_tile_pp(const Tile &t, const float *__restr
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r_w, (FP8Q_LDS void *)(st.w1[b] + (8 * i + wave) * 1024), 16, voff,
                                                koff + (kWN * i + 64) * K32, 0, 0);
   };
-  auto load_sa = [&](int s, float (&dst)[4]) {
+  auto load_sa = [&](int s, float (&dst)[FM]) {
     const int so = (s < KB ? s : KB - 1) * static_cast<int>(M) * 4;
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
+    for (int f = 0; f < FM; ++f)
       dst[f] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsa, sa_off + 64 * f, so, 0));
   };
   // Phase boundary: this wave's LDS reads are complete (lgkmcnt(0)), then the workgroup
@@ -567,15 +571,15 @@ __device__ __forceinline__ void gemm_tile_pp(const Tile &t, const float *__restr
   // copies by their position in that order).
   auto vm_order = [&]() { asm volatile("" ::: "memory"); };
 
-  v8i xf[4], wf[4];
-  v4f pp[4];       // partials of the last fragment column of the previous C phase
-  float sclp[4];   // their scales
+  v8i xf[FM], wf[4];
+  v4f pp[FM];       // partials of the last fragment column of the previous C phase
+  float sclp[FM];   // their scales
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
+  for (int f = 0; f < FM; ++f) {
     pp[f] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     sclp[f] = 0.0f;
   }
-  float saA[4], saB[4];
+  float saA[FM], saB[FM];
   float sb0A = sbrow0[0], sb1A = kOne ? 0.0f : sbrow1[0], sb0B = 0.0f, sb1B = 0.0f;
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
@@ -594,21 +598,21 @@ __device__ __forceinline__ void gemm_tile_pp(const Tile &t, const float *__restr
 
   // C phase over fragment columns j0 .. j0+nc-1 with operands xf, wf; sc0 / sc1: this
   // block's promotion scales of the columns before / from jsplit.
-  auto cphase = [&](int j0, int nc, const float (&sc0)[4], const float (&sc1)[4]) {
+  auto cphase = [&](int j0, int nc, const float (&sc0)[FM], const float (&sc1)[FM]) {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       if (jj >= nc) break;
       const int jp = jj == 0 ? (j0 == 0 ? NFR - 1 : j0 - 1) : j0 + jj - 1;  // column being folded
       const bool first = jp < jsplit;                                       // wave-uniform
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
+      for (int f = 0; f < FM; ++f) {
         const float sf = jj == 0 ? sclp[f] : (kOne || first ? sc0[f] : sc1[f]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[f][jp][i] = __builtin_fmaf(pp[f][i], sf, acc[f][jp][i]);
         pp[f] = mfma_block(wf[jj], xf[f]);
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < FM; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // 4 VALU
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
       }
@@ -616,12 +620,12 @@ __device__ __forceinline__ void gemm_tile_pp(const Tile &t, const float *__restr
     }
     const int jl = j0 + nc - 1;  // the column left for the next phase's first fold
 #pragma unroll
-    for (int f = 0; f < 4; ++f) sclp[f] = kOne || jl < jsplit ? sc0[f] : sc1[f];
+    for (int f = 0; f < FM; ++f) sclp[f] = kOne || jl < jsplit ? sc0[f] : sc1[f];
   };
 
   // One K block kb in buffer buf = kb % 2: sac / sb*c its scales, san / sb*n receive block
   // kb + 1's.
-  auto kstep = [&](int kb, auto buf, float (&sac)[4], float (&san)[4], float &sb0c, float &sb1c, float &sb0n,
+  auto kstep = [&](int kb, auto buf, float (&sac)[FM], float (&san)[FM], float &sb0c, float &sb1c, float &sb0n,
                    float &sb1n) {
     constexpr int b = decltype(buf)::value;
     using Next = std::integral_constant<int, 1 - b>;
@@ -629,7 +633,7 @@ __device__ __forceinline__ void gemm_tile_pp(const Tile &t, const float *__restr
     // for block kb + 1 and the scales of block kb + 1; this block's promotion scales are
     // formed before the barrier so that C0 starts with its first MFMA.
 #pragma unroll
-    for (int f = 0; f < 4; ++f) xf[f] = frag(st.x[b], wm * 4 + f, fo0, fo1);
+    for (int f = 0; f < FM; ++f) xf[f] = frag(st.x[b], wm * FM + f, fo0, fo1);
 #pragma unroll
     for (int j = 0; j < 4; ++j) wf[j] = frag(st.w0[b], wn * 4 + j, fo0, fo1);
     vm_order();
@@ -643,9 +647,9 @@ __device__ __forceinline__ void gemm_tile_pp(const Tile &t, const float *__restr
     // W1 of block kb landed (before phase 4kb+1 ends for either group); issued after it:
     // the scales of kb, X/W0 of kb+1, W1 and the scales of kb+1
     vm_wait<kSA + kXW0 + kW1 + kSA>();
-    float sc0[4], sc1[4];
+    float sc0[FM], sc1[FM];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
+    for (int f = 0; f < FM; ++f) {
       sc0[f] = sac[f] * sb0c;
       sc1[f] = kOne ? sc0[f] : sac[f] * sb1c;
     }
@@ -676,15 +680,15 @@ __device__ __forceinline__ void gemm_tile_pp(const Tile &t, const float *__restr
   if (lead) barrier();  // matches the lagging waves' extra first phase
   vm_wait<0>();         // the copies past the last block (empty) and the scale loads
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
+  for (int f = 0; f < FM; ++f)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[f][NFR - 1][i] = __builtin_fmaf(pp[f][i], sclp[f], acc[f][NFR - 1][i]);
 
-  // Epilogue (as gemm_tile): lane owns row m = m_begin + wm*64 + f*16 + l16 and columns
+  // Epilogue (as gemm_tile): lane owns row m = m_begin + wm*16*FM + f*16 + l16 and columns
   // wc0 + j*16 + 4*kg + {0..3}.
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    const int r = wm * 64 + f * 16 + l16;
+  for (int f = 0; f < FM; ++f) {
+    const int r = wm * 16 * FM + f * 16 + l16;
     if (r >= t.rows) continue;
     const int64_t m = t.m_begin + r;
 #pragma unroll
@@ -812,99 +816,106 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
   return v;
 }
 
-__device__ __forceinline__ int grouped_item(const int32_t *__restrict__ offsets, int G, int64_t M_tot, int64_t N,
-                                            int64_t K, const uint8_t *wq, const float *sb, Tile &t) {
-  const int nt_a = static_cast<int>((N + 255) / 256);
-  const int nt_b = static_cast<int>((N + 511) / 512);
+// Grouped work items with balanced tile heights: expert g's n_g rows, in U = ceil(n_g / 64)
+// units of 64 rows, are cut into m_g = ceil(U / 4) row tiles whose heights (in units, at
+// most 4) differ by at most one: the first U mod m_g tiles get ceil(U / m_g) units, the rest
+// floor(U / m_g) (the last tile holds the remainder of the rows).  So no expert computes more
+// than 63 padding rows, and the tiles of one expert take about the same time.  Tiles are 256
+// columns wide; the m_g tiles of one 256-column weight panel form a group; groups are
+// numbered expert by expert, panel by panel (k = g*P + p, P the number of panels), and
+// group k runs on XCD k mod 8, its tiles consecutively, so that the
+// tiles sharing a weight panel run side by side under one L2 and every XCD gets the same
+// mix of tile heights.  Workgroup b runs on XCD b mod 8 and takes item b / 8 of that XCD's
+// list.  Returns h (the tile's 16-row fragments per wave) or -1 for a surplus workgroup.
+__device__ __forceinline__ int grouped_item(const int32_t *__restrict__ offsets, int G, int64_t M_tot,
+                                                 int64_t N, int64_t K, const uint8_t *wq, const float *sb,
+                                                 Tile &t) {
+  const int P = static_cast<int>((N + 255) / 256);
   const int lane = threadIdx.x & 63;
-  // Expert g's clamped row range [a, b) and its number of work items (lanes past G: 0).
-  auto expert = [&](int g, int64_t &a, int64_t &b) -> int {
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, idx = bid >> 3;
+  // Expert g's clamped row range [a, b), tiles per panel m, its rows in 64-row units u,
+  // and its number of items on this XCD (lanes past G: 0).
+  auto expert = [&](int g, int64_t &a, int64_t &b, int &m, int &u) -> int {
     a = 0;
     b = 0;
+    m = 0;
+    u = 0;
     if (g >= G) return 0;
     a = offsets[g];
     b = offsets[g + 1];
     a = a < 0 ? 0 : (a > M_tot ? M_tot : a);
     b = b < a ? a : (b > M_tot ? M_tot : b);
-    const int64_t n = b - a, full = n / 256, tail = n % 256;
-    return static_cast<int>(full * nt_a + (tail == 0 ? 0 : (tail <= 128 ? nt_b : nt_a)));
+    const int64_t n = b - a;
+    if (n == 0) return 0;
+    m = static_cast<int>((n + 255) / 256);
+    u = static_cast<int>((n + 63) / 64);
+    // groups k in [g*P, g*P + P) with k mod 8 == xcd
+    const int64_t k0 = static_cast<int64_t>(g) * P;
+    const int64_t cnt = (k0 + P - 1 - xcd + 8) / 8 - (k0 - 1 - xcd + 8) / 8;
+    return static_cast<int>(cnt * m);
   };
-  // The experts are scanned 64 at a time, one per lane (the grid bound keeps every count
-  // and the total below 2^31).
-  int total = 0;
-  for (int g0 = 0; g0 < G; g0 += 64) {
-    int64_t a, b;
-    total += __shfl(wave_inclusive_sum(expert(g0 + lane, a, b)), 63);
-  }
-  total = uniform32(total);
-  const int bid = blockIdx.x;
-  if (bid >= total) return -1;
-  const int per = total / 8, rem = total % 8;
-  const int xcd = bid % 8, idx = bid / 8;
-  const int item = xcd * per + (xcd < rem ? xcd : rem) + idx;
   int before = 0;
   for (int g0 = 0; g0 < G; g0 += 64) {
     int64_t a, b;
-    const int cnt = expert(g0 + lane, a, b);
+    int m, u;
+    const int cnt = expert(g0 + lane, a, b, m, u);
     const int incl = wave_inclusive_sum(cnt);
     const int chunk = uniform32(__shfl(incl, 63));
-    if (item < before + chunk) {  // wave-uniform: the expert is in this chunk
-      const int gl = uniform32(__ffsll(static_cast<unsigned long long>(__ballot(before + incl > item))) - 1);
+    if (idx < before + chunk) {  // wave-uniform: the expert is in this chunk
+      const int gl = uniform32(__ffsll(static_cast<unsigned long long>(__ballot(before + incl > idx))) - 1);
       const int g = g0 + gl;
-      const int64_t ga = uniform64(__shfl(a, gl)), gb = uniform64(__shfl(b, gl));
-      int64_t it = uniform64(item - before - (__shfl(incl, gl) - __shfl(cnt, gl)));
+      const int64_t ga = uniform64(__shfl(a, gl));
+      const int64_t n = uniform64(__shfl(b, gl)) - ga;
+      const int mg = uniform32(__shfl(m, gl)), ug = uniform32(__shfl(u, gl));
+      const int r = idx - before - (uniform32(__shfl(incl, gl)) - uniform32(__shfl(cnt, gl)));
+      const int j = r / mg, i = r % mg;  // j-th group of expert g on this XCD, tile i of it
+      const int hq = ug / mg, hr = ug % mg;
+      const int hg = hq + (i < hr ? 1 : 0);          // tile i's height in 64-row units
+      const int u0 = i * hq + (i < hr ? i : hr);     // its first row, in units
+      const int64_t k0 = static_cast<int64_t>(g) * P;
+      const int64_t kfirst = k0 + ((xcd - k0 % 8) + 8) % 8;
+      const int p = static_cast<int>(kfirst + 8 * j - k0);
       t.w = wq + static_cast<int64_t>(g) * N * K;
       t.sb = sb + static_cast<int64_t>(g) * (N / 128) * (K / 128);
       t.n_end = N;
-      const int64_t n = gb - ga, full = n / 256;
-      if (it < full * nt_a) {
-        t.m_begin = ga + (it % full) * 256;
-        t.rows = 256;
-        t.n0 = (it / full) * 256;
-        return 0;
-      }
-      it -= full * nt_a;
-      t.m_begin = ga + full * 256;
-      t.rows = static_cast<int>(n - full * 256);
-      if (t.rows <= 128) {
-        t.n0 = it * 512;
-        return 1;
-      }
-      t.n0 = it * 256;
-      return 0;
+      t.n0 = static_cast<int64_t>(p) * 256;
+      t.m_begin = ga + static_cast<int64_t>(u0) * 64;
+      const int64_t left = n - static_cast<int64_t>(u0) * 64;
+      t.rows = static_cast<int>(left < 64 * hg ? left : 64 * hg);
+      return hg;
     }
     before += chunk;
   }
   return -1;
 }
 
-// Grouped GEMM with both tile shapes in one launch, each on the ping-pong schedule: 256 x 256
-// items with the 4 x 2 wave grid, 128 x 512 items with 2 x 4.  Six LDS arrays (32 + 32 +
-// 16 + 16 + 32 + 32 KB) hold either layout: X in A and W0 in B for 256 x 256 (32 + 16 KB
-// per stage), X in B and W0 in A for 128 x 512 (16 + 32 KB), W1 in C for both.
+// Grouped GEMM on the ping-pong schedule with 256-column tiles of 64, 128, 192 or 256 rows
+// (grouped_item): 16*h rows per wave for h = 1..4, the LDS regions as for dense tiles.
+// The expert tails are short tiles rather than padded ones (their time is mostly the weight
+// panel's stream, which a taller tile would not shorten).
 __global__ __launch_bounds__(kThreads, 1) void gemm_grouped_kernel(
     const uint8_t *__restrict__ xq, const float *__restrict__ sa, const uint8_t *__restrict__ wq,
     const float *__restrict__ sb, const int32_t *__restrict__ offsets, int G, int64_t M, int64_t N,
     int64_t K, void *__restrict__ c, int out_f32) {
-  __shared__ __attribute__((aligned(1024))) uint8_t sa0[32768];
-  __shared__ __attribute__((aligned(1024))) uint8_t sa1[32768];
-  __shared__ __attribute__((aligned(1024))) uint8_t sb0[16384];
-  __shared__ __attribute__((aligned(1024))) uint8_t sb1[16384];
-  __shared__ __attribute__((aligned(1024))) uint8_t sc0[32768];
-  __shared__ __attribute__((aligned(1024))) uint8_t sc1[32768];
-  FP8Q_LDS uint8_t *A0 = (FP8Q_LDS uint8_t *)sa0, *A1 = (FP8Q_LDS uint8_t *)sa1;
-  FP8Q_LDS uint8_t *B0 = (FP8Q_LDS uint8_t *)sb0, *B1 = (FP8Q_LDS uint8_t *)sb1;
-  FP8Q_LDS uint8_t *C0 = (FP8Q_LDS uint8_t *)sc0, *C1 = (FP8Q_LDS uint8_t *)sc1;
+  __shared__ __attribute__((aligned(1024))) uint8_t sx0[32768];
+  __shared__ __attribute__((aligned(1024))) uint8_t sx1[32768];
+  __shared__ __attribute__((aligned(1024))) uint8_t sw00[16384];
+  __shared__ __attribute__((aligned(1024))) uint8_t sw01[16384];
+  __shared__ __attribute__((aligned(1024))) uint8_t sw10[16384];
+  __shared__ __attribute__((aligned(1024))) uint8_t sw11[16384];
+  const PPStages st = {{(FP8Q_LDS uint8_t *)sx0, (FP8Q_LDS uint8_t *)sx1},
+                       {(FP8Q_LDS uint8_t *)sw00, (FP8Q_LDS uint8_t *)sw01},
+                       {(FP8Q_LDS uint8_t *)sw10, (FP8Q_LDS uint8_t *)sw11}};
   Tile t;
-  const int shape = grouped_item(offsets, G, M, N, K, wq, sb, t);
-  if (shape < 0) return;
+  const int h = grouped_item(offsets, G, M, N, K, wq, sb, t);
+  if (h < 0) return;
   t.x = xq;
-  if (shape == 0) {
-    const PPStages st = {{A0, A1}, {B0, B1}, {C0, C1}};
-    gemm_tile_pp<4, 8, true>(t, sa, M, N, K, c, out_f32, st);
-  } else {
-    const PPStages st = {{B0, B1}, {A0, A1}, {C0, C1}};
-    gemm_tile_pp<2, 8, true>(t, sa, M, N, K, c, out_f32, st);
+  switch (h) {
+    case 1: gemm_tile_pp<4, 8, true, 1>(t, sa, M, N, K, c, out_f32, st); break;
+    case 2: gemm_tile_pp<4, 8, true, 2>(t, sa, M, N, K, c, out_f32, st); break;
+    case 3: gemm_tile_pp<4, 8, true, 3>(t, sa, M, N, K, c, out_f32, st); break;
+    default: gemm_tile_pp<4, 8, true, 4>(t, sa, M, N, K, c, out_f32, st); break;
   }
 }
 
@@ -1095,10 +1106,11 @@ hipError_t launch_grouped_gemm(const uint8_t *xq, const float *sa, const uint8_t
   // Upper bound on sum_g ceil(n_g / 256) without reading the offsets on the host.
   const int64_t slots = (M_tot + kBM - 1) / kBM + G;
   const int64_t tiles_n = (N + 255) / 256;
-  if (slots * tiles_n > 0x7fffffff - 4096 || G > 0x7fffffff) return hipErrorInvalidValue;  // item indices stay in int
-  // Upper bound on the number of work items (sum over experts of ceil(n_g/256) rows of
-  // 256-wide tiles) without reading the offsets on the host; surplus workgroups exit.
-  hipLaunchKernelGGL(gemm_grouped_kernel, dim3(static_cast<uint32_t>(slots * tiles_n)), dim3(kThreads), 0, stream,
+  // Each XCD's list holds at most ceil(P/8) groups of every expert (P = tiles_n panels),
+  // so slots * ceil(P/8) items; workgroups past an XCD's list exit.
+  const int64_t grid = 8 * slots * ((tiles_n + 7) / 8);
+  if (grid > 0x7fffffff - 4096 || G > 0x7fffffff) return hipErrorInvalidValue;  // item indices stay in int
+  hipLaunchKernelGGL(gemm_grouped_kernel, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream,
                      xq, sa, wq, sb, offsets, static_cast<int>(G), M_tot, N, K, c, out_f32 ? 1 : 0);
   return hipGetLastError();
 }
