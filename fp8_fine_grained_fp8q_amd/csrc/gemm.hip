@@ -463,19 +463,29 @@ __device__ __forceinline__ void vm_wait() {
 // wave's columns lie in one 128-column weight-scale block (256-wide tiles starting at a
 // multiple of 256), so a fragment row has one promotion scale per K block; otherwise each
 // fragment column picks the scale of its block.
-template <int WM, int NFR, bool kOne, int FM = 4>
+//
+// kVSB (with kOne): the weight-block scale of each K block is fetched with a vector load
+// (uniform across the wave) instead of a scalar load.  Scalar loads share their counter
+// with the LDS reads, so the barrier's lgkmcnt(0) after every phase would also wait for the
+// next block's scale; when that misses in the caches (a grouped tile's expert scales) the
+// wait lands on the critical path.  As a vector load it is one more operation in the
+// fixed per-block sequence, waited for by the compiler before its use a block later.  (The
+// dense kernel keeps the scalar load: its scale rows stay cached, and the vector form
+// measured the same there.)
+template <int WM, int NFR, bool kOne, int FM = 4, bool kVSB = false>
 __device__ __forceinline__ void gemm_tile_pp(const Tile &t, const float *__restrict__ sa, int64_t M, int64_t N,
                                              int64_t K, void *__restrict__ c, int out_f32, const PPStages &st) {
   static_assert(NFR == 7 || NFR == 8, "wave columns 112 or 128");
   static_assert(WM == 4 || (WM == 2 && NFR == 8), "wave grid 4 x 2, or 2 x 4 with 128-column waves");
   static_assert(!kOne || NFR == 8, "one scale block per wave needs 128-column waves");
   static_assert(FM >= 1 && FM <= 4 && (WM * FM) % 4 == 0, "fragment rows per wave 1..4, whole X copies");
+  static_assert(!kVSB || kOne, "vector weight-scale loads: one scale block per wave");
   constexpr int WN = 8 / WM;     // wave columns
   constexpr int kWN = 16 * NFR;  // columns per wave
   constexpr int kNC1 = NFR - 4;  // fragment columns of C1
   // vector memory operations per K block: X/W0 copies, W1 copies, activation scales
   constexpr int kXI = WM * FM / 4;  // X copies per wave (64*WM*FM/4 rows, 8 rows per copy and wave)
-  constexpr int kXW0 = kXI + WN, kW1 = WN, kSA = FM;
+  constexpr int kXW0 = kXI + WN, kW1 = WN, kSA = FM + (kVSB ? 1 : 0);  // kSA: the block's scale loads
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -556,6 +566,14 @@ __device__ __forceinline__ void gemm_tile_pp(const Tile &t, const float *__restr
     for (int f = 0; f < FM; ++f)
       dst[f] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsa, sa_off + 64 * f, so, 0));
   };
+  // kVSB: the weight-block scale of block s (the wave's one scale block), as a vector load
+  const __amdgpu_buffer_rsrc_t rsb =
+      make_rsrc(kVSB ? static_cast<const void *>(sbrow0) : static_cast<const void *>(t.x),
+                kVSB ? static_cast<uint32_t>(KB * 4) : 0u);
+  auto load_sb = [&](int s) -> float {
+    const int kn = s < KB ? s : KB - 1;
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsb, kn * 4, 0, 0));
+  };
   // Phase boundary: this wave's LDS reads are complete (lgkmcnt(0)), then the workgroup
   // barrier.  Written as one asm statement with a memory clobber rather than
   // __syncthreads(), whose workgroup fence would also wait for every direct-to-LDS copy in
@@ -580,7 +598,7 @@ __device__ __forceinline__ void gemm_tile_pp(const Tile &t, const float *__restr
     sclp[f] = 0.0f;
   }
   float saA[FM], saB[FM];
-  float sb0A = sbrow0[0], sb1A = kOne ? 0.0f : sbrow1[0], sb0B = 0.0f, sb1B = 0.0f;
+  float sb0A = kVSB ? 0.0f : sbrow0[0], sb1A = kOne ? 0.0f : sbrow1[0], sb0B = 0.0f, sb1B = 0.0f;
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
 
@@ -590,6 +608,7 @@ __device__ __forceinline__ void gemm_tile_pp(const Tile &t, const float *__restr
   copy_w1(0, B0{});
   vm_order();
   load_sa(0, saA);
+  if constexpr (kVSB) sb0A = load_sb(0);
   vm_order();
   copy_xw0(1, B1{});
   vm_wait<kW1 + kSA + kXW0>();  // X/W0 of block 0 landed (W1 0, the scales, X/W0 1 may be in flight)
@@ -640,10 +659,13 @@ __device__ __forceinline__ void gemm_tile_pp(const Tile &t, const float *__restr
     copy_w1(kb + 1, Next{});
     vm_order();
     load_sa(kb + 1, san);
+    if constexpr (kVSB) sb0n = load_sb(kb + 1);
     vm_order();
-    const int kn = kb + 1 < KB ? kb + 1 : KB - 1;
-    sb0n = sbrow0[kn];
-    if (!kOne) sb1n = sbrow1[kn];
+    if constexpr (!kVSB) {
+      const int kn = kb + 1 < KB ? kb + 1 : KB - 1;
+      sb0n = sbrow0[kn];
+      if (!kOne) sb1n = sbrow1[kn];
+    }
     // W1 of block kb landed (before phase 4kb+1 ends for either group); issued after it:
     // the scales of kb, X/W0 of kb+1, W1 and the scales of kb+1
     vm_wait<kSA + kXW0 + kW1 + kSA>();
@@ -912,10 +934,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_grouped_kernel(
   if (h < 0) return;
   t.x = xq;
   switch (h) {
-    case 1: gemm_tile_pp<4, 8, true, 1>(t, sa, M, N, K, c, out_f32, st); break;
-    case 2: gemm_tile_pp<4, 8, true, 2>(t, sa, M, N, K, c, out_f32, st); break;
-    case 3: gemm_tile_pp<4, 8, true, 3>(t, sa, M, N, K, c, out_f32, st); break;
-    default: gemm_tile_pp<4, 8, true, 4>(t, sa, M, N, K, c, out_f32, st); break;
+    case 1: gemm_tile_pp<4, 8, true, 1, true>(t, sa, M, N, K, c, out_f32, st); break;
+    case 2: gemm_tile_pp<4, 8, true, 2, true>(t, sa, M, N, K, c, out_f32, st); break;
+    case 3: gemm_tile_pp<4, 8, true, 3, true>(t, sa, M, N, K, c, out_f32, st); break;
+    default: gemm_tile_pp<4, 8, true, 4, true>(t, sa, M, N, K, c, out_f32, st); break;
   }
 }
 
