@@ -736,15 +736,64 @@ __device__ __forceinline__ void gemm_tile_pp(const Tile &t, const float *__restr
   }
 }
 
+// Tile `idx` of the rectangle rows [m_lo, m_hi) x columns [n_lo, n_hi) of C cut into tiles
+// of bm rows and 256 columns (m_hi - m_lo a multiple of bm), with dense_tile's XCD-aware
+// raster; the rectangle's first tile index must be a multiple of 8 for the XCD runs to
+// line up (any index is correct).
+__device__ __forceinline__ void region_tile(int idx, int64_t m_lo, int64_t m_hi, int bm, int64_t n_lo,
+                                            int64_t n_hi, const uint8_t *wq, const float *sb, Tile &t) {
+  const int tiles_m = static_cast<int>((m_hi - m_lo) / bm);
+  const int tiles_n = static_cast<int>((n_hi - n_lo + 255) / 256);
+  const int total = tiles_m * tiles_n;
+  const int per = total / 8, rem = total % 8;
+  const int xcd = idx % 8, j = idx / 8;
+  const int logical = xcd * per + (xcd < rem ? xcd : rem) + j;
+  const int span = kGroupM * tiles_n;
+  const int group = logical / span;
+  const int first_m = group * kGroupM;
+  const int gm = min(tiles_m - first_m, kGroupM);
+  const int in_group = logical - group * span;
+  t.m_begin = m_lo + static_cast<int64_t>(first_m + in_group % gm) * bm;
+  t.rows = bm;
+  t.n0 = n_lo + static_cast<int64_t>(in_group / gm) * 256;
+  t.n_end = n_hi;
+  t.w = wq;
+  t.sb = sb;
+}
+
+// Two-region plan of a dense problem (M and N multiples of 256) whose 256 x 256 tiles fill
+// q CU rounds and three quarters (or a half, or a quarter) of one more: region B, rows
+// [0, rb) x columns [0, cb), is cut into one round of tiles of 64*hb rows, and the rest,
+// rows [rb, M) x [0, cb) and all rows x [cb, N), into q whole rounds of 256-row tiles
+// (items 0 .. ta-1; region B takes the last round, item ta + b on workgroup b).  The last
+// round's tiles then do hb/4 of a full tile's work instead of leaving CUs idle.  Returns the
+// item's tile height in units of 64 rows.
+__device__ __forceinline__ int plan_tile(int item, int64_t M, int64_t N, int64_t rb, int64_t cb, int hb,
+                                         const uint8_t *wq, const float *sb, Tile &t) {
+  const int ta1 = static_cast<int>(((M - rb) / 256) * (cb / 256));
+  const int ta2 = static_cast<int>((M / 256) * ((N - cb) / 256));
+  if (item < ta1) {
+    region_tile(item, rb, M, 256, 0, cb, wq, sb, t);
+    return 4;
+  }
+  if (item < ta1 + ta2) {
+    region_tile(item - ta1, 0, M, 256, cb, N, wq, sb, t);
+    return 4;
+  }
+  region_tile(item - ta1 - ta2, 0, rb, 64 * hb, 0, cb, wq, sb, t);
+  return hb;
+}
+
 // Dense problem in 256 x (32*NFR) tiles with the ping-pong schedule, persistent like
-// gemm_blockscaled_split_kernel (workgroup b takes tiles b, b + gridDim.x, ...).
+// gemm_blockscaled_split_kernel (workgroup b takes tiles b, b + gridDim.x, ...); hb > 0
+// selects plan_tile's two-region plan (NFR = 8 only).
 template <int NFR>
 __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(const uint8_t *__restrict__ xq,
                                                               const float *__restrict__ sa,
                                                               const uint8_t *__restrict__ wq,
                                                               const float *__restrict__ sb, int64_t M, int64_t N,
                                                               int64_t K, int total, void *__restrict__ c,
-                                                              int out_f32) {
+                                                              int out_f32, int64_t rb, int64_t cb, int hb) {
   __shared__ __attribute__((aligned(1024))) uint8_t sx0[256 * kBK];
   __shared__ __attribute__((aligned(1024))) uint8_t sx1[256 * kBK];
   __shared__ __attribute__((aligned(1024))) uint8_t sw00[128 * kBK];
@@ -754,12 +803,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(const uint8_t *__r
   const PPStages st = {{(FP8Q_LDS uint8_t *)sx0, (FP8Q_LDS uint8_t *)sx1},
                        {(FP8Q_LDS uint8_t *)sw00, (FP8Q_LDS uint8_t *)sw01},
                        {(FP8Q_LDS uint8_t *)sw10, (FP8Q_LDS uint8_t *)sw11}};
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+  // the full tiles (all of them without a plan), then the plan's last round of short tiles
+  const int full = hb == 0 ? total : total - static_cast<int>(gridDim.x);
+  for (int item = blockIdx.x; item < full; item += gridDim.x) {
     Tile t;
-    dense_tile<32 * NFR>(item, M, 0, N, wq, sb, t);
+    if (NFR != 8 || hb == 0)
+      dense_tile<32 * NFR>(item, M, 0, N, wq, sb, t);
+    else
+      plan_tile(item, M, N, rb, cb, hb, wq, sb, t);
     t.x = xq;
     gemm_tile_pp<4, NFR, NFR == 8>(t, sa, M, N, K, c, out_f32, st);
     __builtin_amdgcn_s_barrier();
+  }
+  if constexpr (NFR == 8) {
+    if (hb == 3) {
+      Tile t;
+      plan_tile(full + static_cast<int>(blockIdx.x), M, N, rb, cb, hb, wq, sb, t);
+      t.x = xq;
+      gemm_tile_pp<4, 8, true, 3>(t, sa, M, N, K, c, out_f32, st);
+    }
   }
 }
 
@@ -1088,15 +1150,40 @@ hipError_t launch_dense(const uint8_t *xq, const float *sa, const uint8_t *wq, c
     const char *wforce = getenv("FP8Q_PP_WIDTH");
     if (wforce && strcmp(wforce, "256") == 0) narrow = false;
     if (wforce && strcmp(wforce, "224") == 0) narrow = true;
-    const int64_t tiles = narrow ? t224 : t256;
+    int64_t tiles = narrow ? t224 : t256;
     if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-    const int64_t grid = min(tiles, slots);
+    // Two-region plan (plan_tile) when the 256 x 256 tiles leave a last round 1/4, 1/2 or
+    // 3/4 full: that round's work as one round of 64*hb-row tiles.  FP8Q_PP_PLAN=off keeps
+    // the uniform tiles.
+    int64_t rb = 0, cb = 0;
+    int hb = 0;
+    const char *pforce = getenv("FP8Q_PP_PLAN");
+    const bool plan_ok = !(pforce && strcmp(pforce, "off") == 0);
+    if (plan_ok && !narrow && M % 256 == 0 && N % 256 == 0 && t256 % slots != 0) {
+      const int64_t r = t256 % slots;
+      for (int h = 3; h >= 3 && hb == 0; --h) {  // 192-row tiles (the kernel's one short form)
+        if (4 * r != h * slots) continue;
+        const int64_t step = h == 3 ? 768 : 256;  // lcm(256, 64h): region A stays 256-row tiled
+        for (int64_t R = (M / step) * step; R >= step; R -= step) {
+          const int64_t area = slots * 64 * h * 256;  // region B's elements
+          if (area % R != 0) continue;
+          const int64_t C = area / R;
+          if (C % 256 != 0 || C > N) continue;
+          rb = R;
+          cb = C;
+          hb = h;
+          break;
+        }
+      }
+      if (hb != 0) tiles = t256 - r + slots;  // q rounds of full tiles and one of region B
+    }
+    const int64_t grid = hb != 0 ? slots : min(tiles, slots);  // the plan needs one workgroup per slot
     if (narrow)
       hipLaunchKernelGGL(gemm_pp_kernel<7>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream, xq, sa, wq,
-                         sb, M, N, K, static_cast<int>(tiles), c, out_f32 ? 1 : 0);
+                         sb, M, N, K, static_cast<int>(tiles), c, out_f32 ? 1 : 0, int64_t(0), int64_t(0), 0);
     else
       hipLaunchKernelGGL(gemm_pp_kernel<8>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream, xq, sa, wq,
-                         sb, M, N, K, static_cast<int>(tiles), c, out_f32 ? 1 : 0);
+                         sb, M, N, K, static_cast<int>(tiles), c, out_f32 ? 1 : 0, rb, cb, hb);
     return hipGetLastError();
   }
   const int64_t tm = (M + kBM - 1) / kBM;

@@ -154,6 +154,29 @@ def test_dense_pingpong_kernel(M, N, K, width, monkeypatch):
     assert np.array_equal(ppbf, spbf)
 
 
+@pytest.mark.parametrize("M,N,K", [(4096, 7168, 128), (4096, 7168, 1024), (3072, 4096, 512), (1024, 4096, 512)])
+def test_dense_two_region_plan(M, N, K, monkeypatch):
+    """The ping-pong kernel's two-region plan: with 256 CUs, 4096x7168 leaves a last round of
+    256 x 256 tiles 3/4 full, which the plan runs as one round of 192-row tiles (rows 3072..
+    of columns 0..4095 and all rows of 4096.. in 256-row tiles first, then rows 0..3071 of
+    columns 0..4095 in 192-row tiles); 3072x4096 is that round alone (192 tiles -> 256 short
+    ones); 1024x4096 (a quarter round) keeps uniform tiles.  Every output against the oracle
+    bound, bit-identical to the uniform tiles (FP8Q_PP_PLAN=off), both output types."""
+    xq, sa, wq, sb = quantized(M, N, K, seed=13 * M + N + K, xscale=2.0)
+    ref = og.gemm_blockscaled(xq, sa, wq, sb)
+    xn, wn = og.row_norms_act(xq, sa), og.row_norms_w(wq, sb)
+    monkeypatch.setenv("FP8Q_DENSE_KERNEL", "pp")
+    plan32 = gpu_gemm(xq, sa, wq, sb, torch.float32)
+    planbf = gpu_gemm(xq, sa, wq, sb)
+    monkeypatch.setenv("FP8Q_PP_PLAN", "off")
+    uni32 = gpu_gemm(xq, sa, wq, sb, torch.float32)
+    unibf = gpu_gemm(xq, sa, wq, sb)
+    assert_gemm_within_tol(plan32, ref, xn, wn, f"plan {M}x{N}x{K} f32")
+    assert_gemm_within_tol(planbf, ref, xn, wn, f"plan {M}x{N}x{K} bf16")
+    assert np.array_equal(plan32, uni32)
+    assert np.array_equal(planbf, unibf)
+
+
 def test_deterministic():
     xq, sa, wq, sb = quantized(300, 640, 512, seed=5)
     a = fq.fp8q_gemm_blockscaled(dev(xq), dev(sa), dev(wq), dev(sb))

@@ -7,7 +7,8 @@ emulations that are about ten times less accurate (scale product or accumulator 
 20 significant bits instead of 24, partials rounded to BF16, a partial folded twice, a
 neighbouring block's scale) break it -- so a K-loop regression of that size cannot pass.
 GPU: the dense, grouped and row-scaled GEMMs meet the bound (FP32 output) on shapes with
-one K block, many K blocks, ragged M and N, and a column split across both tile widths."""
+one K block, many K blocks, ragged M and N, a column split across both tile widths, and
+the ping-pong kernel's short-tile rounds."""
 import numpy as np
 import pytest
 import torch
@@ -98,6 +99,18 @@ def test_gpu_dense_kernels_meet_promotion_bound(kernel, width, monkeypatch):
     c = fq.fp8q_gemm_blockscaled(dev(xq), dev(sa), dev(wq), dev(sb), out_dtype=torch.float32)
     torch.cuda.synchronize()
     pb.check(host(c), C, bound, f"dense kernel {kernel}")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("M,N,K", [(3072, 4096, 512), (4096, 7168, 256)])
+def test_gpu_dense_two_region_plan_meets_promotion_bound(M, N, K):
+    """Shapes the ping-pong kernel runs with a round of 192-row tiles."""
+    import fp8_fine_grained_fp8q_amd as fq
+    from helpers import dev, host
+    xq, sa, wq, sb, C, bound = pb.dense_case(M, N, K, seed=5 * M + N + K)
+    c = fq.fp8q_gemm_blockscaled(dev(xq), dev(sa), dev(wq), dev(sb), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    pb.check(host(c), C, bound, f"dense plan {M}x{N}x{K}")
 
 
 @pytest.mark.gpu
