@@ -816,11 +816,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(const uint8_t *__r
     __builtin_amdgcn_s_barrier();
   }
   if constexpr (NFR == 8) {
-    if (hb == 3) {
+    if (hb != 0) {
       Tile t;
       plan_tile(full + static_cast<int>(blockIdx.x), M, N, rb, cb, hb, wq, sb, t);
       t.x = xq;
-      gemm_tile_pp<4, 8, true, 3>(t, sa, M, N, K, c, out_f32, st);
+      if (hb == 3)
+        gemm_tile_pp<4, 8, true, 3>(t, sa, M, N, K, c, out_f32, st);
+      else if (hb == 2)
+        gemm_tile_pp<4, 8, true, 2>(t, sa, M, N, K, c, out_f32, st);
+      else
+        gemm_tile_pp<4, 8, true, 1>(t, sa, M, N, K, c, out_f32, st);
     }
   }
 }
@@ -1161,7 +1166,7 @@ hipError_t launch_dense(const uint8_t *xq, const float *sa, const uint8_t *wq, c
     const bool plan_ok = !(pforce && strcmp(pforce, "off") == 0);
     if (plan_ok && !narrow && M % 256 == 0 && N % 256 == 0 && t256 % slots != 0) {
       const int64_t r = t256 % slots;
-      for (int h = 3; h >= 3 && hb == 0; --h) {  // 192-row tiles (the kernel's one short form)
+      for (int h = 3; h >= 1 && hb == 0; --h) {
         if (4 * r != h * slots) continue;
         const int64_t step = h == 3 ? 768 : 256;  // lcm(256, 64h): region A stays 256-row tiled
         for (int64_t R = (M / step) * step; R >= step; R -= step) {

@@ -49,7 +49,7 @@
  *  - The dense GEMMs pick their kernel and tile plan from the shape and the CU count.
  *    Environment variables override the choice for testing: FP8Q_DENSE_KERNEL ("pp" or
  *    "split"), FP8Q_PP_WIDTH ("256" or "224") and FP8Q_PP_PLAN ("off": no round of
- *    192-row tiles) for the ping-pong kernel, FP8Q_DENSE_SPLIT ("off", or a count a of
+ *    short tiles) for the ping-pong kernel, FP8Q_DENSE_SPLIT ("off", or a count a of
  *    256-wide tile columns) for the split-plan kernel.  Every kernel and plan gives
  *    bit-identical results.
  */

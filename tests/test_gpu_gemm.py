@@ -154,14 +154,17 @@ def test_dense_pingpong_kernel(M, N, K, width, monkeypatch):
     assert np.array_equal(ppbf, spbf)
 
 
-@pytest.mark.parametrize("M,N,K", [(4096, 7168, 128), (4096, 7168, 1024), (3072, 4096, 512), (1024, 4096, 512)])
+@pytest.mark.parametrize("M,N,K", [(4096, 7168, 128), (4096, 7168, 1024), (3072, 4096, 512), (8192, 7168, 128),
+                                   (2048, 4096, 256), (1024, 4096, 512), (4096, 4096, 256)])
 def test_dense_two_region_plan(M, N, K, monkeypatch):
-    """The ping-pong kernel's two-region plan: with 256 CUs, 4096x7168 leaves a last round of
-    256 x 256 tiles 3/4 full, which the plan runs as one round of 192-row tiles (rows 3072..
-    of columns 0..4095 and all rows of 4096.. in 256-row tiles first, then rows 0..3071 of
-    columns 0..4095 in 192-row tiles); 3072x4096 is that round alone (192 tiles -> 256 short
-    ones); 1024x4096 (a quarter round) keeps uniform tiles.  Every output against the oracle
-    bound, bit-identical to the uniform tiles (FP8Q_PP_PLAN=off), both output types."""
+    """The ping-pong kernel's two-region plan: with 256 CUs a last round of 256 x 256 tiles
+    that is 3/4, 1/2 or 1/4 full runs as one round of 192-, 128- or 64-row tiles.  4096x7168
+    (448 tiles): rows 3072.. of columns 0..4095 and all rows of 4096.. in 256-row tiles,
+    then rows 0..3071 of columns 0..4095 in 192-row tiles; 3072x4096 (192 tiles) is that
+    round alone; 8192x7168 (896 tiles) ends in 128-row tiles; 2048x4096 (128) and 1024x4096
+    (64) become one round of 128- and 64-row tiles; 4096x4096 (256 tiles, one whole round)
+    keeps uniform tiles.  Every output against the oracle bound, bit-identical to the
+    uniform tiles (FP8Q_PP_PLAN=off), both output types."""
     xq, sa, wq, sb = quantized(M, N, K, seed=13 * M + N + K, xscale=2.0)
     ref = og.gemm_blockscaled(xq, sa, wq, sb)
     xn, wn = og.row_norms_act(xq, sa), og.row_norms_w(wq, sb)

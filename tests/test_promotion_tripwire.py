@@ -102,9 +102,9 @@ def test_gpu_dense_kernels_meet_promotion_bound(kernel, width, monkeypatch):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("M,N,K", [(3072, 4096, 512), (4096, 7168, 256)])
+@pytest.mark.parametrize("M,N,K", [(3072, 4096, 512), (4096, 7168, 256), (2048, 4096, 256), (1024, 4096, 512)])
 def test_gpu_dense_two_region_plan_meets_promotion_bound(M, N, K):
-    """Shapes the ping-pong kernel runs with a round of 192-row tiles."""
+    """Shapes the ping-pong kernel runs with a round of 192-, 128- or 64-row tiles."""
     import fp8_fine_grained_fp8q_amd as fq
     from helpers import dev, host
     xq, sa, wq, sb, C, bound = pb.dense_case(M, N, K, seed=5 * M + N + K)
