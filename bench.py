@@ -275,7 +275,8 @@ def vendor_context(torch, M, N, K, steps):
     """hipBLASLt's FP8 GEMM on the same shape through torch._scaled_mm (E4M3 operands, BF16
     out; one scale per tensor, then one per row and column): mean microseconds of `steps`
     back-to-back launches after 20 untimed ones.  Context only: neither form applies
-    per-128-K block scales."""
+    per-128-K block scales.  This library's block-scaled GEMM is timed the same way on the
+    same codes (every tile and block scale 1.0; the FP32 promotion still runs every 128 K)."""
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev).manual_seed(0)
     a = (torch.randn(M, K, device=dev, generator=g) * 50).to(torch.float8_e4m3fn)
@@ -301,6 +302,24 @@ def vendor_context(torch, M, N, K, steps):
             out[f"hipblaslt_scaled_mm_{kind}_tflops"] = round(2.0 * M * N * K / us / 1e6, 1)
         except Exception as ex:  # pragma: no cover - depends on the installed torch
             out[f"hipblaslt_scaled_mm_{kind}"] = f"unavailable: {type(ex).__name__}"
+    import fp8_fine_grained_fp8q_amd as fq
+    xq, wq = a.view(torch.uint8), b.view(torch.uint8)
+    s_act = torch.ones(K // 128, M, device=dev)
+    s_w = torch.ones(N // 128, K // 128, device=dev)
+    c = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(20):
+        fq.fp8q_gemm_blockscaled(xq, s_act, wq, s_w, out=c, stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        fq.fp8q_gemm_blockscaled(xq, s_act, wq, s_w, out=c, stream=stream)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1e3
+    out["fp8q_gemm_blockscaled_same_codes_us"] = round(us, 1)
+    out["fp8q_gemm_blockscaled_same_codes_tflops"] = round(2.0 * M * N * K / us / 1e6, 1)
     return out
 
 
