@@ -46,7 +46,6 @@ FP8 peak.  `cpu_baseline` times the CPU oracle on a bounded sample of the same w
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -109,8 +108,10 @@ def gen(workload: str):
 
 
 def source_hash() -> str:
-    with open(GEMM_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """The GEMM source's code hash (comments and blank lines removed), the key of the
+    committed counter and traffic summaries."""
+    from fp8_fine_grained_fp8q_amd.srchash import code_hash
+    return code_hash(GEMM_SOURCE)
 
 
 def measured_traffic(workload: str):

@@ -14,15 +14,17 @@ number of XCD instances it is summed over, found from its ratio to the traced du
   coexec         = sum SQ_VALU_MFMA_COEXEC_CYCLES / (SIMD_NUM * CUs * gui_cycles)
   lds_bank_conflict = sum SQ_LDS_BANK_CONFLICT / (CUs * gui_cycles)
   wait_lds_share = SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES ; wait_any_share = SQ_WAIT_ANY / SQ_WAVE_CYCLES
-The GEMM source hash is stored so that the benchmark reports these only while the kernel
-is unchanged.
+The GEMM source's code hash (fp8_fine_grained_fp8q_amd/srchash.py: comments and blank
+lines removed) is stored so that the benchmark reports these only while the kernel code is
+unchanged.
 """
 import csv
 import glob
-import hashlib
 import json
 import os
 import sys
+
+from fp8_fine_grained_fp8q_amd.srchash import code_hash
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GEMM_SOURCE = os.path.join(ROOT, "fp8_fine_grained_fp8q_amd", "csrc", "gemm.hip")
@@ -90,7 +92,7 @@ def main():
                         ("SQ_ACTIVE_INST_LDS", "active_lds_share")):
             if k in c:
                 res[name] = round(c[k] / c["SQ_WAVE_CYCLES"], 4)
-    res["gemm_source_sha256_16"] = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()[:16]
+    res["gemm_source_sha256_16"] = code_hash(GEMM_SOURCE)
     try:
         data = json.load(open(out))
     except (OSError, ValueError):

@@ -16,13 +16,18 @@
 //
 // Workgroup tile 256(M) x BN(N) with BN = 32*NFR, K step 128 (= the scale block), 8 waves
 // in a 4(M) x 2(N) grid, each owning 64 x 16*NFR outputs (4*NFR*4 FP32 accumulator VGPRs).
-// Dense problems use 256-wide tiles, or a column split into a 256-wide range followed by a
-// 192-wide range in the same launch when that fills the GPU's CUs in fewer rounds.  The MFMA
-// takes the weight fragment as its A operand and the activation fragment as B, so every
-// lane owns one output row m and four consecutive columns n: one activation scale per
-// fragment row and 8- or 16-byte output stores.
+// Two kernels share this layout.  The ping-pong kernel (gemm_tile_pp, the dense default and
+// the grouped kernel) has the two waves of each SIMD take turns between LDS reads and
+// MFMAs; its tiles are 256 wide and 256 rows tall, or 64/128/192 rows for the grouped
+// kernel's expert tails and for a dense problem's last round of tiles.  The split-plan
+// kernel (gemm_tile, the row-scaled weight-gradient GEMM) runs one barrier per K step and
+// uses 256-wide tiles, or a 256-wide column range followed by a 192-wide one in the same
+// launch when that fills the GPU's CUs in fewer rounds.  The MFMA takes the weight
+// fragment as its A operand and the activation fragment as B, so every lane owns one
+// output row m and four consecutive columns n: one activation scale per fragment row and
+// 8- or 16-byte output stores.
 //
-// Operand staging: both stages live in LDS, double buffered.  gfx950's buffer_load ... lds
+// Operand staging: the stages live in LDS, double buffered.  gfx950's buffer_load ... lds
 // moves 16 B per lane from global memory straight into LDS, lane p's bytes landing at 16p
 // of a 1 KB block, from any global address; each group of 8 lanes fetches one 128-byte
 // K block of one row.  Layout of a stage, per group of 16 rows (2 KB): rows r and r+8 of

@@ -10,10 +10,11 @@ dispatch (other copies in the run are input uploads and buffer clones of other s
     python -m fp8_fine_grained_fp8q_amd.traffic_summary WORKLOAD FETCH_CSV WRITE_CSV
 """
 import csv
-import hashlib
 import json
 import os
 import sys
+
+from fp8_fine_grained_fp8q_amd.srchash import code_hash
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GEMM_SOURCE = os.path.join(ROOT, "fp8_fine_grained_fp8q_amd", "csrc", "gemm.hip")
@@ -61,7 +62,7 @@ def main():
         "read_bytes_per_launch": round(rd), "write_bytes_per_launch": round(wr),
         "bytes_per_launch": round(rd + wr),
     }
-    sha = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()[:16]
+    sha = code_hash(GEMM_SOURCE)
     try:
         data = json.load(open(OUT))
     except (OSError, ValueError):
