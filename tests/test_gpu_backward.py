@@ -52,7 +52,7 @@ def test_weight_quant_transposed_matches_plain_quantizer():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1].view(torch.int32), b[1].view(torch.int32))
 
 
-@pytest.mark.parametrize("M,K", [(128, 128), (256, 384), (640, 256)])
+@pytest.mark.parametrize("M,K", [(128, 128), (256, 384), (640, 256), (384, 1152)])
 def test_act_quant_dual(M, K):
     rng = np.random.default_rng(M + K)
     x = rng.standard_normal((M, K)) * np.logspace(-2, 2, K)[None, :]
