@@ -20,9 +20,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfp8q.so")
 SOURCES = ["quant.hip", "gemm.hip", "moe.hip", "fp8q_abi.cpp"]
-# Streaming-bandwidth probes the benchmark reads the quantizers against (not part of the path).
+# Streaming-bandwidth and unit-rate probes the kernels are read against (not part of the path).
 PROBE_LIB = os.path.join(HERE, "libfp8q_probe.so")
-PROBE_SOURCES = ["stream_probe.hip"]
+PROBE_SOURCES = ["stream_probe.hip", "unit_probe.hip"]
 ARCH = "gfx950"
 
 
