@@ -209,3 +209,23 @@ def test_moe_entry_point_argument_checks(lib):
     assert c(A, 0, 8, 64, A, A, 0, 2, 0, 0, None) == E["FP8Q_OK"]           # no tokens
     assert c(A, 0, 8, 64, 0, A, 4, 2, A, 0, None) == E["FP8Q_ERR_NULL"]
     assert c(A, 0, 8, 64, A, A, 4, 2, A + 2, 0, None) == E["FP8Q_ERR_ALIGN"]
+
+
+def test_probe_library_exports_and_rejects_bad_arguments():
+    """The measurement probes (libfp8q_probe.so, not part of the path) load, export their
+    entry points, and reject bad arguments before any HIP call."""
+    path = os.path.join(ROOT, "fp8_fine_grained_fp8q_amd", "libfp8q_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("probe library not built")
+    probe = ctypes.CDLL(path)
+    for name in ("probe_copy", "probe_read2_write1", "probe_lds_read", "probe_lds_copy", "probe_mfma"):
+        getattr(probe, name).restype = ctypes.c_int
+    invalid = 1  # hipErrorInvalidValue
+    null = ctypes.c_void_p(0)
+    assert probe.probe_copy(null, null, ctypes.c_int64(0), null) == invalid
+    assert probe.probe_read2_write1(null, null, ctypes.c_int64(-1), null) == invalid
+    assert probe.probe_lds_read(256, 0, null, null, null) == invalid
+    assert probe.probe_lds_copy(0, 256, 0, null, null, null, null) == invalid
+    assert probe.probe_lds_copy(3, 256, 10, null, null, null, null) == invalid
+    assert probe.probe_mfma(5, 256, 10, null, null, null) == invalid
+    assert probe.probe_mfma(0, 0, 10, null, null, null) == invalid
