@@ -18,6 +18,11 @@
 //       (L2-resident after the first pass), at most 16 in flight: mode 0 buffer_load ... lds
 //       with 16 bytes per lane into a 64 KB LDS array, mode 1 the same with 4 bytes per
 //       lane, mode 2 16-byte loads into registers (folded into the checksum)
+//   probe_lds_mix(burst, blocks, iters_r, iters_c, src, out, cyc, stream)
+//       waves 0-3 read LDS in bursts of `burst` (8 or 16) one-KB ds_read_b128, each burst
+//       waited for before use, while waves 4-7 copy as probe_lds_copy mode 0, into
+//       separate 64 KB arrays (128 KB of static LDS: one workgroup per CU); cyc holds four
+//       values per workgroup, the readers' cycles and ticks, then the copiers'
 //   probe_mfma(mode, blocks, iters, out, cyc, stream)
 //       v_mfma_f32_16x16x128_f8f6f4 on register operands (random finite E4M3 codes, 4 row
 //       and 4 column fragments per wave): mode 0 8 MFMAs per iteration chained through C;
@@ -117,6 +122,67 @@ __global__ __launch_bounds__(kProbeThreads) void lds_copy_kernel(const uint8_t *
   __syncthreads();
   record(cyc, t0, r0);
   out[blockIdx.x * kProbeThreads + tid] = acc ^ reinterpret_cast<const uint32_t *>(lds)[tid];
+}
+
+// Waves 0-3 read LDS as lds_read_kernel does (from one 64 KB array) while waves 4-7 copy
+// into another 64 KB array as lds_copy_kernel<0> does; each half times its own loop
+// (readers: cyc[4b], cyc[4b+1]; copiers: cyc[4b+2], cyc[4b+3]).  iters_r or iters_c = 0
+// leaves that half idle.
+template <int BURST>
+__global__ __launch_bounds__(kProbeThreads) void lds_mix_kernel(const uint8_t *src, uint32_t *out,
+                                                                unsigned long long *cyc, int iters_r, int iters_c) {
+  __shared__ __attribute__((aligned(16))) uint32_t rbuf[16384];  // 64 KB read by waves 0-3
+  __shared__ __attribute__((aligned(1024))) uint8_t cbuf[65536];  // 64 KB written by waves 4-7
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  for (int i = tid; i < 16384; i += kProbeThreads) {
+    rbuf[i] = i * 2654435761u;
+    reinterpret_cast<uint32_t *>(cbuf)[i] = 0u;
+  }
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(src), (short)0, 512 * 1024, 0x00020000);
+  uint32_t acc0 = 0x03020100u, acc1 = 0x07060504u;
+  __syncthreads();
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  if (wave < 4) {
+    // BURST reads of one KB each, all issued before the first is used (a memory phase's
+    // pattern); bytes 16*(64*wave + lane) + 1024*u, u < BURST: below 20 KB
+    const char *base = reinterpret_cast<const char *>(rbuf) + (wave * 64 + lane) * 16;
+    for (int it = 0; it < iters_r; ++it) {
+      asm volatile("" ::: "memory");
+      uint4 v[BURST];
+#pragma unroll
+      for (int u = 0; u < BURST; ++u) v[u] = *reinterpret_cast<const uint4 *>(base + u * 1024);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int u = 0; u < BURST; u += 2) {
+        acc0 = __builtin_amdgcn_perm(v[u].x ^ v[u].y, v[u].z ^ v[u].w, acc0);
+        acc1 = __builtin_amdgcn_perm(v[u + 1].x ^ v[u + 1].y, v[u + 1].z ^ v[u + 1].w, acc1);
+      }
+    }
+  } else {
+    const int cw = wave - 4;  // copier 0..3: LDS slots 16*cw + i of 64
+    for (int it = 0; it < iters_c; ++it) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int blk = ((it * 8 + i) * 4 + cw) & 511;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (PROBE_LDS void *)(cbuf + (16 * cw + 2 * i + (it & 1)) * 1024), 16,
+                                                 lane * 16, blk * 1024, 0, 0);
+      }
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+  if (lane == 0 && (wave == 0 || wave == 4)) {
+    const int o = wave == 0 ? 0 : 2;
+    cyc[4 * blockIdx.x + o] = t1 - t0;
+    cyc[4 * blockIdx.x + o + 1] = r1 - r0;
+  }
+  __syncthreads();
+  out[blockIdx.x * kProbeThreads + tid] = acc0 ^ acc1 ^ reinterpret_cast<const uint32_t *>(cbuf)[tid];
 }
 
 template <int MODE>
@@ -241,6 +307,19 @@ extern "C" int probe_lds_copy(int mode, int blocks, int iters, const void *src, 
     case 1: return launch_probe(lds_copy_kernel<1>, kPadLdsProbe, blocks, s, p, o, c, iters);
     case 2: return launch_probe(lds_copy_kernel<2>, kPadLdsProbe, blocks, s, p, o, c, iters);
   }
+  return static_cast<int>(hipErrorInvalidValue);
+}
+
+extern "C" int probe_lds_mix(int burst, int blocks, int iters_r, int iters_c, const void *src, void *out,
+                             void *cyc, void *stream) {
+  if (iters_r < 0 || iters_c < 0 || iters_r > (1 << 24) || iters_c > (1 << 24) || iters_r + iters_c == 0)
+    return static_cast<int>(hipErrorInvalidValue);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint8_t *p = static_cast<const uint8_t *>(src);
+  uint32_t *o = static_cast<uint32_t *>(out);
+  unsigned long long *c = static_cast<unsigned long long *>(cyc);
+  if (burst == 8) return launch_probe(lds_mix_kernel<8>, size_t(0), blocks, s, p, o, c, iters_r, iters_c);
+  if (burst == 16) return launch_probe(lds_mix_kernel<16>, size_t(0), blocks, s, p, o, c, iters_r, iters_c);
   return static_cast<int>(hipErrorInvalidValue);
 }
 

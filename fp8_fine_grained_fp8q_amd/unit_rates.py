@@ -29,7 +29,7 @@ def _lib():
     if not os.path.exists(PROBE_LIB):
         raise RuntimeError(f"{PROBE_LIB} not built (python -m fp8_fine_grained_fp8q_amd.build)")
     lib = ctypes.CDLL(PROBE_LIB)
-    for f in (lib.probe_lds_read, lib.probe_lds_copy, lib.probe_mfma):
+    for f in (lib.probe_lds_read, lib.probe_lds_copy, lib.probe_lds_mix, lib.probe_mfma):
         f.restype = ctypes.c_int
     return lib
 
@@ -43,7 +43,7 @@ def run() -> dict:
     dev = torch.device("cuda:0")
     blocks = torch.cuda.get_device_properties(dev).multi_processor_count
     out = torch.zeros(blocks * THREADS, dtype=torch.int32, device=dev)
-    cyc = torch.zeros(2 * blocks, dtype=torch.int64, device=dev)
+    cyc = torch.zeros(4 * blocks, dtype=torch.int64, device=dev)
     src = torch.randint(0, 256, (512 * 1024,), dtype=torch.uint8, device=dev,
                         generator=torch.Generator(device=dev).manual_seed(5))
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -55,7 +55,7 @@ def run() -> dict:
             if rc != 0:
                 raise RuntimeError(f"probe launch failed ({rc})")
             torch.cuda.synchronize()
-        c = cyc.cpu().view(blocks, 2).double()
+        c = cyc[: 2 * blocks].cpu().view(blocks, 2).double()
         return c[:, 0], c[:, 1] * 10.0  # cycles, ns
 
     res = {"cus": blocks, "waves_per_cu": THREADS // 64}
@@ -73,6 +73,26 @@ def run() -> dict:
                      "GBs_per_cu": round(_median(byts / ns), 1),
                      "TBs_chip": round(_median(byts / ns) * blocks / 1000, 2),
                      "ghz": round(_median(cy / ns), 3)}
+    # 4 waves reading LDS (bursts of 8 or 16 one-KB reads, each waited for) beside 4 waves
+    # copying into it, each half alone and both together
+    ic = 1800
+    cases = [(8, "lds_read_4_waves_burst8_alone", 8192, 0), (16, "lds_read_4_waves_burst16_alone", 4096, 0),
+             (8, "lds_copy_4_waves_alone", 0, ic), (8, "lds_read_burst8_and_copy_together", 8192, ic),
+             (16, "lds_read_burst16_and_copy_together", 4096, ic)]
+    for burst, name, a, b in cases:
+        for _ in range(2):
+            rc = lib.probe_lds_mix(burst, blocks, a, b, ctypes.c_void_p(src.data_ptr()), p_out, p_cyc, stream)
+            if rc != 0:
+                raise RuntimeError(f"probe launch failed ({rc})")
+            torch.cuda.synchronize()
+        c = cyc.cpu().view(blocks, 4).double()
+        entry = {}
+        if a:
+            entry["read_bytes_per_clk_cu"] = round(_median(4 * a * burst * 1024 / c[:, 0]), 1)
+        if b:
+            entry["copy_bytes_per_clk_cu"] = round(_median(4 * b * 8 * 1024 / c[:, 2]), 1)
+        entry["ghz"] = round(_median(c[:, 0 if a else 2] / (c[:, 1 if a else 3] * 10.0)), 3)
+        res[name] = entry
     names = {0: "mfma_chained", 1: "mfma_plus_4_independent_fma", 2: "mfma_promotion_one_column_behind",
              3: "mfma_promotion_at_once", 4: "mfma_promotion_one_column_behind_interleaved"}
     for mode in (0, 1, 2, 3, 4):

@@ -218,7 +218,7 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     if not os.path.exists(path):
         pytest.skip("probe library not built")
     probe = ctypes.CDLL(path)
-    for name in ("probe_copy", "probe_read2_write1", "probe_lds_read", "probe_lds_copy", "probe_mfma"):
+    for name in ("probe_copy", "probe_read2_write1", "probe_lds_read", "probe_lds_copy", "probe_lds_mix", "probe_mfma"):
         getattr(probe, name).restype = ctypes.c_int
     invalid = 1  # hipErrorInvalidValue
     null = ctypes.c_void_p(0)
@@ -227,5 +227,7 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     assert probe.probe_lds_read(256, 0, null, null, null) == invalid
     assert probe.probe_lds_copy(0, 256, 0, null, null, null, null) == invalid
     assert probe.probe_lds_copy(3, 256, 10, null, null, null, null) == invalid
+    assert probe.probe_lds_mix(8, 256, 0, 0, null, null, null, null) == invalid
+    assert probe.probe_lds_mix(12, 256, 10, 10, null, null, null, null) == invalid
     assert probe.probe_mfma(5, 256, 10, null, null, null) == invalid
     assert probe.probe_mfma(0, 0, 10, null, null, null) == invalid
