@@ -34,7 +34,10 @@
  *    the current HIP device; the caller owns all buffers and keeps them alive until
  *    the work on `stream` completes.  Outputs must not alias inputs.
  *  - `stream` is a hipStream_t passed as void*; NULL means the default stream.
- *    Calls are asynchronous on it and never synchronize the host.
+ *    Calls are asynchronous on it and never synchronize the host.  Without FP8Q_DEBUG a
+ *    call issues only kernel launches on `stream` (no allocation, memset, copy or wait),
+ *    so it can be captured into a HIP graph and replayed; the GEMMs read the CU count
+ *    once per device outside any stream, so make one call before capturing.
  *  - Arguments are checked before any HIP call; a failed check returns a negative
  *    fp8q_status and launches nothing.  M == 0 (or M_tot == 0) is a no-op FP8Q_OK.
  *  - Base pointers must be 16-byte aligned.  K and N must be multiples of 128.  The GEMMs
