@@ -882,14 +882,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_blockscaled_split_kernel(
   }
 }
 
-// Grouped GEMM work items.  Expert g (rows offsets[g] .. offsets[g+1]-1, clamped to
-// [0, M_tot)) is cut into floor(n_g / 256) full 256-row tiles, each covering N in 256-wide
-// tiles, plus its tail of n_g mod 256 rows: a tail of at most 128 rows uses 128 x 512 tiles
-// (the same per-wave work, half as many tiles as 256 x 256 ones would need), a longer tail
-// one more row of 256 x 256 tiles.  Items are numbered expert by expert, N tile by N tile,
-// M tile last (tiles of one expert sharing a weight panel are adjacent), and workgroups are
-// dealt to the 8 XCDs in contiguous runs of items.  Returns the tile shape (0: 256 x 256,
-// 1: 128 x 512) or -1 past the last item.
 // A value the caller knows to be equal in every lane, moved to a scalar register (so tile
 // coordinates derived from lane shuffles still address the operands through SGPRs).
 __device__ __forceinline__ int uniform32(int v) { return __builtin_amdgcn_readfirstlane(v); }
