@@ -81,8 +81,8 @@ WORKLOADS = {
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="continue the untimed warm-up steps until this many ms of them have run")
     ap.add_argument("--clock-seconds", type=float, default=2.0,
