@@ -6,7 +6,7 @@ these tests do not depend on the GPU quantizers.  Cases: the tiny workload, ragg
 spanning several 256x256 tiles with partial tails in M and N, an exactly representable
 integer case (bit-exact, pins the MFMA operand and output layouts), a characterisation of
 the matrix core's own block summation, the dense 4096x7168x7168
-workload in the benchmarked launch (every output), grouped MoE shapes with
+workload in the benchmarked launch (every output), a 65536-long contraction (512 K blocks), grouped MoE shapes with
 empty / 1 / 127..257-row experts and with 65..256 experts (several offset-scan chunks), the
 MoE up/down workloads (every expert on sampled column blocks; four experts in full), run-to-run
 determinism, the dense tile plans (uniform 256-wide tiles or a 256/192-wide column split,
@@ -50,7 +50,7 @@ def test_tiny(out_dtype):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (17, 384, 256), (255, 256, 640), (257, 640, 384),
-                                   (300, 1152, 1024), (513, 384, 128), (64, 2304, 896)])
+                                   (300, 1152, 1024), (513, 384, 128), (64, 2304, 896), (130, 256, 65536)])
 def test_ragged_shapes(M, N, K):
     xq, sa, wq, sb = quantized(M, N, K, seed=M + N + K, xscale=3.0)
     ref = og.gemm_blockscaled(xq, sa, wq, sb)

@@ -7,7 +7,7 @@ emulations that are about ten times less accurate (scale product or accumulator 
 20 significant bits instead of 24, partials rounded to BF16, a partial folded twice, a
 neighbouring block's scale) break it -- so a K-loop regression of that size cannot pass.
 GPU: the dense, grouped and row-scaled GEMMs meet the bound (FP32 output) on shapes with
-one K block, many K blocks, ragged M and N, a column split across both tile widths, and
+one K block, many K blocks (up to 512), ragged M and N, a column split across both tile widths, and
 the ping-pong kernel's short-tile rounds."""
 import numpy as np
 import pytest
@@ -78,7 +78,7 @@ def test_tripwire_is_far_tighter_than_the_acceptance_bound():
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("M,N,K", [(96, 256, 128), (257, 640, 384), (300, 1152, 1024), (512, 512, 7168),
-                                   (1, 128, 2048), (600, 2304, 896)])
+                                   (1, 128, 2048), (600, 2304, 896), (64, 256, 65536)])
 def test_gpu_dense_meets_promotion_bound(M, N, K):
     import fp8_fine_grained_fp8q_amd as fq
     from helpers import dev, host
